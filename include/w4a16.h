@@ -1,0 +1,116 @@
+/*
+ * w4a16.h - C ABI of the W4A16 fused dequantize-GEMM library for MI355X (gfx950).
+ *
+ * Operation ("4.3 Weight-only INT4", section 1, W4A16 storage and compute; section 4,
+ * Marlin): y[M,N] = x[M,K] * W_hat[K,N], where W_hat is rebuilt on-chip from 4-bit codes
+ * and per-group metadata, multiplied with 16-bit activations, accumulated in fp32.
+ * K is the reduction axis (input features), N the output features.
+ *
+ *   affine:  W_hat[k,n] = RN_t((q[k,n] - z[k/g,n]) * s[k/g,n])     (one rounding)
+ *   NF4:     W_hat[k,n] = RN_t(c[q[k,n]] * a[k/64,n])
+ *
+ * with t the activation type (fp16 or bf16), RN round-to-nearest-even, q the 4-bit code,
+ * s the group scale, z the 4-bit zero-point (8 when qzeros is NULL: symmetric codes
+ * -8..7 stored offset-binary), c a 16-entry fp16 codebook and a an fp16 absmax.
+ *
+ * Canonical input formats ("INT4 and Low-Bit Inference", section 6-9, packed layout):
+ *   qweight  int32 [K/8][N]     eight codes along K per word, code j in bits 4j..4j+3
+ *   scales   t     [K/g][N]     one scale per group of g consecutive k, per column
+ *   qzeros   int32 [K/g][N/8]   eight zero-points along N per word, same nibble order
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees or synchronizes; all work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the null stream) and is complete only when the caller synchronizes it.
+ *   - Arrays are dense and row-major. x, out and the packed weight need 16-byte aligned
+ *     base addresses; scales 2-byte; qzeros 4-byte.
+ *   - Arguments are checked on the host before anything is enqueued. A bad argument
+ *     returns W4A16_ERR_ARG, a shape the kernels do not implement W4A16_ERR_UNSUPPORTED;
+ *     nothing is launched in either case. A failed launch returns W4A16_ERR_HIP.
+ *     Faults during execution surface at the caller's next synchronization.
+ *   - There is no slow or CPU fallback path.
+ *   - No global mutable state: calls on different streams may run concurrently.
+ *
+ * Supported shapes: K % 32 == 0, K % group_size == 0, N % 16 == 0, M >= 0, K, N > 0,
+ * group_size in {32, 64, 128}; K * N < 2^34 (packed weight below 8 GiB).
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1, W4A16_F32 = 2 } w4a16_dtype;
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_ARG = 1,          /* null pointer, misalignment, inconsistent shape or dtype */
+  W4A16_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (e.g. N % 16 != 0)    */
+  W4A16_ERR_HIP = 3           /* the HIP runtime rejected a launch                       */
+} w4a16_status;
+
+/* Bytes of the device-layout weight for a K x N matrix: K_pad * N / 2 with
+ * K_pad = K rounded up to a multiple of 128. Returns 0 for unsupported shapes. */
+size_t w4a16_packed_bytes(int K, int N);
+
+/* Load-time re-layout of the weight codes ("INT4 and Low-Bit Inference", section 5,
+ * Marlin's tricks: weights are re-ordered once at load so run-time unpacking is
+ * branch-free and reads are coalesced; "4.3 Weight-only INT4", section 4).
+ *   qweight   [in]  canonical int32 [K/8][N]
+ *   packed    [out] w4a16_packed_bytes(K, N) bytes; an opaque order private to this
+ *                   library, read only by the GEMM and dequant entry points below.
+ * Must not alias qweight. */
+w4a16_status w4a16_pack(const int32_t* qweight, int K, int N, int32_t* packed, void* stream);
+
+/* The W4A16 GEMM with affine (asymmetric) or symmetric INT4 weights.
+ *   x         [in]  act [M][K], act = W4A16_F16 or W4A16_BF16
+ *   packed    [in]  output of w4a16_pack for this K, N
+ *   scales    [in]  act [K/group_size][N]
+ *   qzeros    [in]  int32 [K/group_size][N/8], or NULL for symmetric codes (zero 8)
+ *   out       [out] out_dtype [M][N], out_dtype = act or W4A16_F32
+ * M = 0 is a no-op. Results are deterministic (no atomics in the reduction). */
+w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
+                        const int32_t* packed, const void* scales, const int32_t* qzeros,
+                        int group_size, void* out, w4a16_dtype out_dtype, void* stream);
+
+/* The W4A16 GEMM with NF4 weights ("INT4 and Low-Bit Inference", section 5, The formats;
+ * "INT4", section INT4, FP4, and NF4 are not identical).
+ *   absmax    [in]  fp16 [K/block_size][N] per-block absmax scales
+ *   codebook  [in]  16 fp16 values (device memory), code i -> codebook[i]
+ *   block_size      32, 64 or 128
+ * Other arguments as for w4a16_gemm. */
+w4a16_status w4a16_gemm_nf4(const void* x, int M, int K, int N, w4a16_dtype act,
+                            const int32_t* packed, const uint16_t* absmax,
+                            const uint16_t* codebook, int block_size, void* out,
+                            w4a16_dtype out_dtype, void* stream);
+
+/* Test hook: write W_hat[K][N] (row-major, in `wdtype` = F16 or BF16) using the same
+ * device dequantization routine the GEMM kernels use. scales are in wdtype. */
+w4a16_status w4a16_dequant(const int32_t* packed, const void* scales, const int32_t* qzeros,
+                           int K, int N, int group_size, w4a16_dtype wdtype, void* w_out,
+                           void* stream);
+
+/* Test hook: NF4 counterpart of w4a16_dequant (absmax and codebook are fp16). */
+w4a16_status w4a16_dequant_nf4(const int32_t* packed, const uint16_t* absmax,
+                               const uint16_t* codebook, int K, int N, int block_size,
+                               w4a16_dtype wdtype, void* w_out, void* stream);
+
+/* Name of the kernel w4a16_gemm / w4a16_gemm_nf4 launch for this shape (static string),
+ * so a caller can log which path ran ("4.3 Weight-only INT4", section 4.1). */
+const char* w4a16_kernel_name(int M, int K, int N, int group_size);
+
+/* Static description of a status code. */
+const char* w4a16_status_string(w4a16_status status);
+
+/* Library version string. */
+const char* w4a16_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -27,7 +27,7 @@ def _pack8(codes: np.ndarray, axis: int) -> np.ndarray:
     word = np.zeros((c.shape[0], *c.shape[2:]), dtype=np.uint32)
     for j in range(8):
         word |= c[:, j] << np.uint32(4 * j)
-    return np.moveaxis(word, 0, axis).view(np.int32)
+    return np.ascontiguousarray(np.moveaxis(word, 0, axis)).view(np.int32)
 
 
 def _unpack8(words: np.ndarray, axis: int) -> np.ndarray:
@@ -36,7 +36,7 @@ def _unpack8(words: np.ndarray, axis: int) -> np.ndarray:
     for j in range(8):
         out[:, j] = (w >> np.uint32(4 * j)) & np.uint32(0xF)
     out = out.reshape(w.shape[0] * 8, *w.shape[1:])
-    return np.moveaxis(out, 0, axis)
+    return np.ascontiguousarray(np.moveaxis(out, 0, axis))
 
 
 def pack_codes(q: np.ndarray) -> np.ndarray:

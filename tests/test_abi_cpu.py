@@ -1,0 +1,125 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from weight_only_int4_w4a16_amd import binding
+    return binding.lib()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for n in ("w4a16_pack", "w4a16_gemm", "w4a16_gemm_nf4", "w4a16_dequant",
+              "w4a16_dequant_nf4", "w4a16_packed_bytes", "w4a16_kernel_name",
+              "w4a16_status_string", "w4a16_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in include/w4a16.h but not exported"
+
+
+def test_packed_bytes(L):
+    from weight_only_int4_w4a16_amd import packed_bytes
+    assert packed_bytes(4096, 4096) == 4096 * 4096 // 2
+    assert packed_bytes(352, 48) == 384 * 48 // 2          # K padded to a multiple of 128
+    assert packed_bytes(4096, 24) == 0                      # N % 16 != 0
+    assert packed_bytes(0, 16) == 0
+    assert packed_bytes(8192, 57344) == 8192 * 57344 // 2
+
+
+def _gemm(L, x=1, M=1, K=4096, N=4096, act=0, packed=16, scales=16, qzeros=16, g=128,
+          out=16, odt=0):
+    vp = ctypes.c_void_p
+    return L.w4a16_gemm(vp(x) if x else None, M, K, N, act, vp(packed) if packed else None,
+                        vp(scales) if scales else None, vp(qzeros) if qzeros else None, g,
+                        vp(out) if out else None, odt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=100), 1),              # K % 8
+    (dict(K=4096 + 32, g=128), 1), # K % g
+    (dict(g=48), 1),               # group size not in {32, 64, 128}
+    (dict(N=4100), 1),             # N % 8
+    (dict(N=4104), 2),             # N % 16: well-formed, not implemented
+    (dict(M=-1), 1),
+    (dict(act=2), 1),              # fp32 activations
+    (dict(act=0, odt=1), 1),       # bf16 out for fp16 activations
+    (dict(x=0), 1),                # null x
+    (dict(packed=0), 1),
+    (dict(scales=0), 1),
+    (dict(out=0), 1),
+    (dict(x=8), 1),                # misaligned x (needs 16 bytes)
+    (dict(scales=3), 1),           # misaligned scales
+    (dict(qzeros=2), 1),           # misaligned zeros
+])
+def test_gemm_rejects_bad_arguments_before_launch(L, kw, status):
+    assert _gemm(L, **kw) == status
+
+
+def test_gemm_m0_is_a_noop(L):
+    assert _gemm(L, M=0, x=0, packed=0, scales=0, out=0) == 0
+
+
+def test_nf4_requires_codebook(L):
+    vp = ctypes.c_void_p
+    st = L.w4a16_gemm_nf4(vp(16), 1, 4096, 4096, 0, vp(16), vp(16), None, 64, vp(16), 0, None)
+    assert st == 1
+
+
+def test_pack_and_dequant_reject_bad_arguments(L):
+    vp = ctypes.c_void_p
+    assert L.w4a16_pack(vp(16), 100, 4096, vp(32), None) == 1
+    assert L.w4a16_pack(vp(16), 4096, 24, vp(32), None) == 2
+    assert L.w4a16_pack(vp(16), 4096, 4096, vp(16), None) == 1      # aliasing
+    assert L.w4a16_pack(None, 4096, 4096, vp(16), None) == 1
+    assert L.w4a16_dequant(vp(16), vp(16), None, 4096, 4096, 128, 2, vp(16), None) == 1
+    assert L.w4a16_dequant_nf4(vp(16), vp(16), None, 4096, 4096, 64, 0, vp(16), None) == 1
+
+
+def test_kernel_name_and_strings(L):
+    from weight_only_int4_w4a16_amd import kernel_name, version
+    assert kernel_name(1, 4096, 4096, 128).startswith("w4a16_skinny")
+    assert kernel_name(0, 4096, 4096, 128) == "none"
+    for s in range(4):
+        assert L.w4a16_status_string(s)
+    assert version()
+
+
+def test_oracle_and_product_share_no_code():
+    """The oracle imports nothing from the product package and vice versa (the seeded
+    input module ``synth`` is the one shared piece and holds none of the method)."""
+    prod = os.path.join(ROOT, "weight_only_int4_w4a16_amd")
+    orc = os.path.join(ROOT, "oracle")
+    for d, banned in ((orc, r"weight_only_int4_w4a16_amd|synth"), (prod, r"\boracle\b")):
+        for dirpath, _, files in os.walk(d):
+            for f in files:
+                if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h", ".c")):
+                    text = open(os.path.join(dirpath, f)).read()
+                    code = re.sub(r'""".*?"""', "", text, flags=re.S)
+                    imports = [ln for ln in code.splitlines()
+                               if re.match(r"\s*(import|from|#include)\b", ln)]
+                    for ln in imports:
+                        assert not re.search(banned, ln), f"{f}: {ln}"
+
+
+def test_synth_module_holds_no_method_arithmetic():
+    src = open(os.path.join(ROOT, "weight_only_int4_w4a16_amd", "synth.py")).read()
+    for banned in ("rint", "clip(", "matmul", "@", "dequant", "<< np.uint32(4"):
+        assert banned not in src.split('"""', 2)[-1], banned

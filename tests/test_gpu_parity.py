@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+* dequantized weights: bit-exact (uint16 patterns) on ragged shapes, every format;
+* GEMM: max|y - y_ref| <= 1e-3 max|y_ref| (fp64 oracle), element by element on sizes
+  the oracle finishes in seconds (several strips, ragged M and K), and on sampled
+  16-column strips at the full sizes of the benchmarked workloads;
+* exact special cases: one-hot rows reproduce W_hat bit for bit, power-of-two scales with
+  small-integer activations give exact sums; bf16 output equals RNE of fp32 output;
+  repeated runs are bit-identical.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_int4_w4a16_amd import synth
+
+from gpu_common import (assert_close, device_inputs, from_dev, oracle_columns, out_values,
+                        require_gpu, rtn_case, run_gemm, sample_strips, to_dev, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ bit-exact dequant
+
+@pytest.mark.parametrize("K,N,g,act,fmt", [
+    (256, 32, 128, "f16", "asym"),
+    (352, 48, 32, "f16", "asym"),      # ragged K: last 128-block has 3 of 4 steps
+    (320, 64, 64, "f16", "asym"),
+    (384, 16, 128, "f16", "sym"),
+    (4096, 4096, 128, "f16", "asym"),  # the single-GEMV workload, whole matrix
+    (288, 32, 32, "bf16", "asym"),
+    (512, 48, 128, "bf16", "sym"),
+    (448, 32, 64, "f16", "nf4"),
+    (256, 32, 64, "bf16", "nf4"),
+])
+def test_dequant_bit_exact(K, N, g, act, fmt):
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    _announce(f"dequant K={K} N={N} g={g} {act} {fmt}")
+    c = rtn_case(1, K, N, g, act, sym=(fmt == "sym"), seed=K + N, nf4=(fmt == "nf4"))
+    d = device_inputs(c)
+    if fmt == "nf4":
+        wt = w4.dequant_nf4(d["packed"], d["scales"], d["codebook"], K, g,
+                            torch.float16 if act == "f16" else torch.bfloat16)
+    else:
+        wt = w4.dequant(d["packed"], d["scales"], d["qzeros"], K, g)
+    torch.cuda.synchronize()
+    got = from_dev(wt)
+    exp = c["w_hat"]
+    got_bits = got.view(np.uint16) if got.dtype == np.float16 else got
+    exp_bits = exp.view(np.uint16) if exp.dtype == np.float16 else exp
+    bad = np.argwhere(got_bits != exp_bits)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+# ------------------------------------------------------------------ small GEMMs, all outputs
+
+SMALL = [
+    # M, K, N, g, act, fmt
+    (1, 512, 256, 128, "f16", "asym"),
+    (3, 352, 48, 32, "f16", "asym"),
+    (16, 1024, 128, 64, "f16", "asym"),
+    (17, 512, 64, 128, "f16", "asym"),
+    (33, 256, 96, 32, "f16", "asym"),
+    (64, 512, 64, 128, "f16", "asym"),
+    (100, 384, 80, 128, "f16", "asym"),
+    (1, 1024, 64, 128, "f16", "sym"),
+    (8, 640, 32, 128, "f16", "sym"),
+    (1, 512, 64, 128, "bf16", "asym"),
+    (5, 288, 48, 32, "bf16", "asym"),
+    (40, 512, 32, 64, "bf16", "sym"),
+    (1, 512, 64, 64, "f16", "nf4"),
+    (12, 448, 48, 64, "f16", "nf4"),
+    (2, 256, 32, 64, "bf16", "nf4"),
+    (70, 256, 32, 64, "f16", "nf4"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,g,act,fmt", SMALL)
+def test_gemm_small_all_outputs(M, K, N, g, act, fmt):
+    torch = torch_mod()
+    _announce(f"gemm M={M} K={K} N={N} g={g} {act} {fmt}")
+    c = rtn_case(M, K, N, g, act, sym=(fmt == "sym"), seed=7 * M + K, nf4=(fmt == "nf4"))
+    d = device_inputs(c)
+    y_ref = oracle.gemm_ref(c["x"], c["w_hat"], act)
+    y32 = run_gemm(c, d, out_dtype=torch.float32)
+    assert_close(from_dev(y32).astype(np.float64), y_ref, "fp32 out")
+    y16 = run_gemm(c, d)
+    if act == "f16":
+        assert_close(out_values(from_dev(y16), torch.float16), y_ref, "fp16 out")
+    else:
+        # bf16 output is the nearest-even rounding of the same fp32 accumulation
+        exp = oracle.round_nearest_bf16_bits(from_dev(y32).astype(np.float64))
+        assert np.array_equal(from_dev(y16), exp)
+
+
+def test_gemm_m0_is_noop():
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    c = rtn_case(1, 256, 32, 128)
+    d = device_inputs(c)
+    x0 = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    y = w4.gemm(x0, d["packed"], d["scales"], d["qzeros"], 128)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 32)
+
+
+# ------------------------------------------------------------------ exact special cases
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_one_hot_rows_reproduce_w_hat_exactly(act):
+    torch = torch_mod()
+    _announce(f"one-hot {act}")
+    K, N = 384, 64
+    c = rtn_case(1, K, N, 128, act, seed=99)
+    ks = np.array([0, 1, 7, 8, 127, 128, 200, 383])
+    x = np.zeros((len(ks), K), np.float32)
+    x[np.arange(len(ks)), ks] = 1.0
+    c["x"] = x.astype(np.float16) if act == "f16" else synth.f32_to_bf16_bits(x)
+    c["M"] = len(ks)
+    d = device_inputs(c)
+    y = from_dev(run_gemm(c, d))
+    exp = c["w_hat"][ks]
+    assert np.array_equal(y.view(np.uint16) if act == "f16" else y,
+                          exp.view(np.uint16) if act == "f16" else exp)
+
+
+def test_power_of_two_scales_integer_activations_exact():
+    torch = torch_mod()
+    _announce("pow2 exact")
+    rng = np.random.default_rng(5)
+    M, K, N, g = 7, 1024, 64, 32
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    z = rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)
+    e = rng.integers(3, 7, size=(K // g, N))
+    s = (2.0 ** -e).astype(np.float16)
+    xi = rng.integers(-3, 4, size=(M, K))
+    c = {"M": M, "K": K, "N": N, "g": g, "act": "f16", "nf4": False,
+         "x": xi.astype(np.float16), "qweight": oracle.pack_codes(q), "scales": s,
+         "qzeros": oracle.pack_zeros(z)}
+    d = device_inputs(c)
+    y = from_dev(run_gemm(c, d, out_dtype=torch.float32)).astype(np.float64)
+    w_hat = oracle.dequant_affine(c["qweight"], s, c["qzeros"], g)
+    y_ref = oracle.gemm_ref(c["x"], w_hat)
+    # every partial sum is a multiple of 2**-6 below 2**24 * 2**-6: exact in fp32
+    assert np.array_equal(y, y_ref)
+
+
+def test_repeat_runs_are_bit_identical():
+    torch = torch_mod()
+    c = rtn_case(16, 2048, 256, 128, seed=3)
+    d = device_inputs(c)
+    a = from_dev(run_gemm(c, d, out_dtype=torch.float32))
+    b = from_dev(run_gemm(c, d, out_dtype=torch.float32))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------------ the single-GEMV workload
+
+def test_single_gemv_4096x4096_all_outputs():
+    """x fp16 [1,4096], W [4096,4096] ~ N(0, 0.02) asymmetric g128: every output."""
+    torch = torch_mod()
+    _announce("single GEMV 4096x4096")
+    c = rtn_case(1, 4096, 4096, 128, "f16", seed=synth.seed_for(1, 0, 0))
+    d = device_inputs(c)
+    y_ref = oracle.gemm_ref(c["x"], c["w_hat"])
+    assert_close(out_values(from_dev(run_gemm(c, d)), torch.float16), y_ref, "fp16 out")
+    assert_close(from_dev(run_gemm(c, d, torch.float32)).astype(np.float64), y_ref, "fp32 out")
+
+
+# ------------------------------------------------------------------ full sizes, sampled strips
+
+FULL = []
+for (K, N) in ((4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096)):   # 8B-shaped, g128
+    for M in (1, 4, 16):
+        FULL.append((M, K, N, 128, "f16", "asym"))
+for (K, N) in ((8192, 10240), (8192, 8192), (8192, 57344), (28672, 8192)):  # 70B-shaped, sym
+    for M in (1, 8, 32):
+        FULL.append((M, K, N, 128, "f16", "sym"))
+for M in (1, 2, 4, 8, 16, 32, 64, 128, 256):                                # crossover sweep
+    FULL.append((M, 4096, 14336, 128, "f16", "asym"))
+    FULL.append((M, 4096, 14336, 32, "f16", "asym"))
+    FULL.append((M, 4096, 14336, 64, "f16", "nf4"))
+FULL.append((2048, 8192, 28672, 128, "bf16", "asym"))                       # prefill-shaped
+
+
+@pytest.mark.parametrize("M,K,N,g,act,fmt", FULL)
+def test_full_size_sampled_strips(M, K, N, g, act, fmt):
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    _announce(f"full M={M} K={K} N={N} g={g} {act} {fmt} kernel={w4.kernel_name(M, K, N, g)}")
+    seed = synth.seed_for(9, K // 128 + N // 1024, 0)
+    qweight, scales, qzeros = synth.timing_weights(K, N, g, seed, symmetric=(fmt != "asym"),
+                                                   scale_dtype=act)
+    x = synth.activations(M, K, seed + synth.ROLE_X, act)
+    case = {"M": M, "K": K, "N": N, "g": g, "act": act, "nf4": fmt == "nf4", "x": x,
+            "qweight": qweight, "scales": scales, "qzeros": qzeros}
+    if fmt == "nf4":
+        case["codebook"] = oracle.nf4_codebook()
+        case["scales"] = synth.random_scales(K // g, N, seed + 7, "f16", 0.02, 0.09)
+    d = device_inputs(case)
+    cols = sample_strips(N, 6, seed)
+    y_ref = oracle_columns(x, qweight, case["scales"], qzeros, g, act, cols,
+                           nf4=case["nf4"], codebook=case.get("codebook"))
+    y = from_dev(run_gemm(case, d, out_dtype=torch.float32)).astype(np.float64)
+    assert_close(y[:, cols], y_ref, "fp32 out, sampled strips")
+    del d
+    torch.cuda.empty_cache()

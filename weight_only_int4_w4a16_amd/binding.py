@@ -1,0 +1,173 @@
+"""ctypes binding over ``libw4a16.so`` (the C ABI in ``include/w4a16.h``).
+
+Argument marshalling only: tensors are passed as device pointers with the caller's
+current HIP stream; every step of the computation runs in the library's HIP kernels.
+The library is loaded on first use and a missing or unloadable library raises
+:class:`W4A16Error`; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4a16.so")
+
+F16, BF16, F32 = 0, 1, 2
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+
+_lib = None
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libw4a16.so`` once; raise if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise W4A16Error(f"{LIB_PATH} is missing: build it with "
+                         "`python -m weight_only_int4_w4a16_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.w4a16_packed_bytes.argtypes = [i32, i32]
+    L.w4a16_packed_bytes.restype = sz
+    L.w4a16_pack.argtypes = [vp, i32, i32, vp, vp]
+    L.w4a16_pack.restype = i32
+    L.w4a16_gemm.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp]
+    L.w4a16_gemm.restype = i32
+    L.w4a16_gemm_nf4.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp]
+    L.w4a16_gemm_nf4.restype = i32
+    L.w4a16_dequant.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    L.w4a16_dequant.restype = i32
+    L.w4a16_dequant_nf4.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    L.w4a16_dequant_nf4.restype = i32
+    L.w4a16_kernel_name.argtypes = [i32, i32, i32, i32]
+    L.w4a16_kernel_name.restype = ctypes.c_char_p
+    L.w4a16_status_string.argtypes = [i32]
+    L.w4a16_status_string.restype = ctypes.c_char_p
+    L.w4a16_version.argtypes = []
+    L.w4a16_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        msg = lib().w4a16_status_string(status).decode()
+        raise W4A16Error(f"{what}: {msg} (status {status})", status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    m = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+    if t not in m:
+        raise W4A16Error(f"unsupported dtype {t}")
+    return m[t]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise W4A16Error("tensors must be contiguous device tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def packed_bytes(K: int, N: int) -> int:
+    return int(lib().w4a16_packed_bytes(K, N))
+
+
+def pack(qweight):
+    """Canonical ``qweight[K/8, N]`` int32 -> the library's device layout (int32 tensor)."""
+    torch = _torch()
+    if qweight.dtype != torch.int32 or qweight.dim() != 2:
+        raise W4A16Error("qweight must be a 2-D int32 tensor [K/8, N]")
+    K, N = qweight.shape[0] * 8, qweight.shape[1]
+    nb = packed_bytes(K, N)
+    if nb == 0:
+        raise W4A16Error(f"unsupported shape K={K} N={N}", ERR_UNSUPPORTED)
+    out = torch.empty(nb // 4, dtype=torch.int32, device=qweight.device)
+    _check(lib().w4a16_pack(_ptr(qweight), K, N, _ptr(out), _stream(qweight)), "w4a16_pack")
+    return out
+
+
+def gemm(x, packed, scales, qzeros, group_size: int, out_dtype=None, out=None):
+    """``y = x @ W_hat`` with affine (``qzeros`` given) or symmetric (``qzeros=None``) INT4.
+
+    ``x[M, K]`` fp16/bf16, ``scales[K/g, N]`` in x's dtype, ``qzeros[K/g, N/8]`` int32.
+    """
+    torch = _torch()
+    M, K = x.shape
+    N = scales.shape[1]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if scales.dtype != x.dtype:
+        raise W4A16Error("scales must have the activation dtype")
+    st = lib().w4a16_gemm(_ptr(x), M, K, N, _dt(x.dtype), _ptr(packed), _ptr(scales),
+                          _ptr(qzeros), group_size, _ptr(out), _dt(out.dtype), _stream(x))
+    _check(st, "w4a16_gemm")
+    return out
+
+
+def gemm_nf4(x, packed, absmax, codebook, block_size: int = 64, out_dtype=None, out=None):
+    """``y = x @ W_hat`` with NF4 weights: fp16 ``absmax[K/b, N]``, fp16 ``codebook[16]``."""
+    torch = _torch()
+    M, K = x.shape
+    N = absmax.shape[1]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if absmax.dtype != torch.float16 or codebook.dtype != torch.float16:
+        raise W4A16Error("NF4 absmax and codebook are fp16")
+    st = lib().w4a16_gemm_nf4(_ptr(x), M, K, N, _dt(x.dtype), _ptr(packed), _ptr(absmax),
+                              _ptr(codebook), block_size, _ptr(out), _dt(out.dtype), _stream(x))
+    _check(st, "w4a16_gemm_nf4")
+    return out
+
+
+def dequant(packed, scales, qzeros, K: int, group_size: int):
+    """Test hook: W_hat[K, N] in the scales' dtype, from the GEMM's own dequant routine."""
+    torch = _torch()
+    N = scales.shape[1]
+    w = torch.empty((K, N), dtype=scales.dtype, device=scales.device)
+    st = lib().w4a16_dequant(_ptr(packed), _ptr(scales), _ptr(qzeros), K, N, group_size,
+                             _dt(scales.dtype), _ptr(w), _stream(scales))
+    _check(st, "w4a16_dequant")
+    return w
+
+
+def dequant_nf4(packed, absmax, codebook, K: int, block_size: int = 64, wdtype=None):
+    """Test hook: NF4 W_hat[K, N] (fp16 by default, or bf16)."""
+    torch = _torch()
+    N = absmax.shape[1]
+    wdtype = torch.float16 if wdtype is None else wdtype
+    w = torch.empty((K, N), dtype=wdtype, device=absmax.device)
+    st = lib().w4a16_dequant_nf4(_ptr(packed), _ptr(absmax), _ptr(codebook), K, N, block_size,
+                                 _dt(wdtype), _ptr(w), _stream(absmax))
+    _check(st, "w4a16_dequant_nf4")
+    return w
+
+
+def kernel_name(M: int, K: int, N: int, group_size: int) -> str:
+    return lib().w4a16_kernel_name(M, K, N, group_size).decode()
+
+
+def version() -> str:
+    return lib().w4a16_version().decode()

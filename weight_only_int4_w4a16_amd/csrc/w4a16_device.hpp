@@ -1,0 +1,250 @@
+// w4a16_device.hpp - device-side building blocks shared by every W4A16 kernel on gfx950:
+// the private packed weight layout, nibble unpacking, the one-rounding dequantization and
+// thin MFMA wrappers. Every kernel that produces W_hat calls the routines below, so the
+// dequant test hook and the GEMMs compute bit-identical weights.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w4a16_launch.hpp"
+
+namespace w4a16 {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+
+// ---------------------------------------------------------------------------------------
+// Packed device layout (written by the pack kernel, read by GEMM and dequant kernels).
+//
+// The weight is cut into blocks of 128 k x 16 n (KC = ceil(K/128) blocks per column
+// strip, NT = N/16 strips). Block (nt, kc) is 1 KiB at word offset (nt*KC + kc)*256:
+// lane l (0..63) of a wave owns 16 bytes, words 4l..4l+3; word j of lane l holds the 8
+// codes of column n = 16*nt + l%16 at k = 128*kc + 32*j + 8*(l/16) + i, i = 0..7.
+// That is exactly the B operand a lane feeds to v_mfma_f32_16x16x32 for k-step j of the
+// block, so one 16-byte load per lane brings four MFMA steps and a wave reads 1 KiB
+// contiguously. Codes past K are zero-filled.
+//
+// Within a word the codes are stored in nibble order [q0 q2 q4 q6 q1 q3 q5 q7] so the
+// fp16 unpack below needs one shift and four and-or operations for eight codes.
+// ---------------------------------------------------------------------------------------
+__host__ __device__ inline uint32_t permute_nibbles(uint32_t canon) {
+  // canonical code i sits in nibble i; device nibble p holds code perm[p],
+  // perm = {0, 2, 4, 6, 1, 3, 5, 7}
+  uint32_t out = 0;
+  out |= ((canon >> 0) & 0xFu) << 0;
+  out |= ((canon >> 8) & 0xFu) << 4;
+  out |= ((canon >> 16) & 0xFu) << 8;
+  out |= ((canon >> 24) & 0xFu) << 12;
+  out |= ((canon >> 4) & 0xFu) << 16;
+  out |= ((canon >> 12) & 0xFu) << 20;
+  out |= ((canon >> 20) & 0xFu) << 24;
+  out |= ((canon >> 28) & 0xFu) << 28;
+  return out;
+}
+
+__host__ __device__ inline size_t block_word_offset(int nt, int kc, int KC) {
+  return ((size_t)nt * KC + kc) * 256;
+}
+
+// ---------------------------------------------------------------------------------------
+// fp16 dequantization of one packed word: W_hat = RN_fp16((q - z) * s).
+//
+// Magic-number unpack: OR-ing a code into the mantissa of 0x6400 (1024.0) gives 1024 + q
+// exactly; a code shifted up by 4 bits into 0x5400 (64.0) gives 64 + q exactly (the
+// mantissa step of 64.0 is 1/16). Subtracting 1024 + z or 64 + z (exact in fp16: both are
+// integers below 2048) leaves q - z exactly, and one packed multiply by s rounds once.
+// ---------------------------------------------------------------------------------------
+struct ZeroF16 {
+  uint32_t c1024;  // half2 (1024 + z, 1024 + z)
+  uint32_t c64;    // half2 (64 + z, 64 + z)
+};
+
+__device__ inline ZeroF16 make_zero_f16(uint32_t z) {
+  ZeroF16 r;
+  r.c1024 = (0x6400u | z) * 0x00010001u;
+  r.c64 = (0x5400u | (z << 4)) * 0x00010001u;
+  return r;
+}
+
+__device__ inline h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+
+// (a & mask) | c as one gfx950 v_bitop3_b32. The 8-bit immediate is the truth table of
+// the function over (src0, src1, src2) with the conventional operand patterns 0xF0, 0xCC,
+// 0xAA: (0xF0 & 0xCC) | 0xAA = 0xEA. Left to itself the compiler emits v_and + v_or.
+__device__ inline uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+  constexpr uint32_t A = 0xF0, B = 0xCC, C = 0xAA;
+  return __builtin_amdgcn_bitop3_b32(a, mask, c, (A & B) | C);
+}
+
+__device__ inline h8_t dequant_word_f16(uint32_t w, ZeroF16 zc, h2_t s2) {
+  const uint32_t w8 = w >> 8;
+  const uint32_t v0 = and_or(w, 0x000F000Fu, 0x64006400u);   // (q0, q1) + 1024
+  const uint32_t v1 = and_or(w, 0x00F000F0u, 0x54005400u);   // (q2, q3) + 64
+  const uint32_t v2 = and_or(w8, 0x000F000Fu, 0x64006400u);  // (q4, q5) + 1024
+  const uint32_t v3 = and_or(w8, 0x00F000F0u, 0x54005400u);  // (q6, q7) + 64
+  const h2_t d0 = (as_h2(v0) - as_h2(zc.c1024)) * s2;
+  const h2_t d1 = (as_h2(v1) - as_h2(zc.c64)) * s2;
+  const h2_t d2 = (as_h2(v2) - as_h2(zc.c1024)) * s2;
+  const h2_t d3 = (as_h2(v3) - as_h2(zc.c64)) * s2;
+  h8_t r;
+  r[0] = d0[0]; r[1] = d0[1]; r[2] = d1[0]; r[3] = d1[1];
+  r[4] = d2[0]; r[5] = d2[1]; r[6] = d3[0]; r[7] = d3[1];
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------
+// bf16 dequantization of one packed word: W_hat = RN_bf16((q - z) * s).
+//
+// Codes are spread into bytes and converted with v_cvt_f32_ubyte*. In fp32,
+// fma(q, s, -(z*s)) is exact: z*s and (q - z)*s are products of a 4/5-bit integer and an
+// 8-bit significand, so both are representable and the fused result needs no rounding.
+// The single rounding is the fp32 -> bf16 conversion (nearest-even).
+// ---------------------------------------------------------------------------------------
+struct ZeroF32 {
+  float s;
+  float nzs;  // -(z * s), exact
+};
+
+__device__ inline ZeroF32 make_zero_f32(uint32_t z, float s) {
+  ZeroF32 r;
+  r.s = s;
+  r.nzs = -((float)z * s);
+  return r;
+}
+
+__device__ inline b8_t dequant_word_bf16(uint32_t w, ZeroF32 zs) {
+  // device nibble p holds code perm[p]; lo bytes = nibbles 0,2,4,6 = codes 0,4,1,5;
+  // hi bytes = nibbles 1,3,5,7 = codes 2,6,3,7
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  float q[8];
+  q[0] = (float)(lo & 0xFFu);
+  q[4] = (float)((lo >> 8) & 0xFFu);
+  q[1] = (float)((lo >> 16) & 0xFFu);
+  q[5] = (float)(lo >> 24);
+  q[2] = (float)(hi & 0xFFu);
+  q[6] = (float)((hi >> 8) & 0xFFu);
+  q[3] = (float)((hi >> 16) & 0xFFu);
+  q[7] = (float)(hi >> 24);
+  b8_t r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)__builtin_fmaf(q[i], zs.s, zs.nzs);
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------
+// NF4 dequantization: W_hat = RN_t(c[q] * a). The 16 fp16 levels live in registers as
+// two byte tables (low and high bytes of each level); v_perm_b32 looks up four codes at
+// once from eight bytes, a bit-3 select picks the half of the table.
+// ---------------------------------------------------------------------------------------
+struct Nf4Lut {
+  uint32_t lo[4];  // low bytes of levels 0..15, four per word
+  uint32_t hi[4];  // high bytes
+};
+
+__device__ inline uint32_t perm_b32(uint32_t hi_word, uint32_t lo_word, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi_word, lo_word, sel);
+}
+
+// idx: four byte-lane indices 0..15 -> four table bytes
+__device__ inline uint32_t lut16_bytes(const uint32_t t[4], uint32_t idx) {
+  const uint32_t sel = idx & 0x07070707u;
+  const uint32_t a = perm_b32(t[1], t[0], sel);          // entries 0..7
+  const uint32_t b = perm_b32(t[3], t[2], sel);          // entries 8..15
+  const uint32_t m = ((idx >> 3) & 0x01010101u) * 0xFFu;  // 0xFF where idx >= 8
+  return (a & ~m) | (b & m);
+}
+
+// four codes (one per byte of idx) -> two half2 words holding levels (b0,b1), (b2,b3)
+__device__ inline void lut16_half(const Nf4Lut& L, uint32_t idx, uint32_t& h01, uint32_t& h23) {
+  const uint32_t lo = lut16_bytes(L.lo, idx);
+  const uint32_t hi = lut16_bytes(L.hi, idx);
+  h01 = perm_b32(hi, lo, 0x05010400u);  // bytes: lo0, hi0, lo1, hi1
+  h23 = perm_b32(hi, lo, 0x07030602u);  // bytes: lo2, hi2, lo3, hi3
+}
+
+__device__ inline h8_t dequant_word_nf4_f16(uint32_t w, const Nf4Lut& L, h2_t a2) {
+  // lo bytes: codes 0,4,1,5 ; hi bytes: codes 2,6,3,7 -> regroup to (0,1),(2,3),(4,5),(6,7)
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t i0 = perm_b32(hi, lo, 0x06040200u);  // codes 0,1,2,3
+  const uint32_t i1 = perm_b32(hi, lo, 0x07050301u);  // codes 4,5,6,7
+  uint32_t c01, c23, c45, c67;
+  lut16_half(L, i0, c01, c23);
+  lut16_half(L, i1, c45, c67);
+  const h2_t d0 = as_h2(c01) * a2;
+  const h2_t d1 = as_h2(c23) * a2;
+  const h2_t d2 = as_h2(c45) * a2;
+  const h2_t d3 = as_h2(c67) * a2;
+  h8_t r;
+  r[0] = d0[0]; r[1] = d0[1]; r[2] = d1[0]; r[3] = d1[1];
+  r[4] = d2[0]; r[5] = d2[1]; r[6] = d3[0]; r[7] = d3[1];
+  return r;
+}
+
+__device__ inline b8_t dequant_word_nf4_bf16(uint32_t w, const Nf4Lut& L, float a) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t i0 = perm_b32(hi, lo, 0x06040200u);
+  const uint32_t i1 = perm_b32(hi, lo, 0x07050301u);
+  uint32_t c[4];
+  lut16_half(L, i0, c[0], c[1]);
+  lut16_half(L, i1, c[2], c[3]);
+  b8_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const h2_t h = as_h2(c[p]);
+    // fp16 level * fp16 absmax: exact in fp32 (11 x 11 significant bits); one rounding
+    r[2 * p] = (__bf16)((float)h[0] * a);
+    r[2 * p + 1] = (__bf16)((float)h[1] * a);
+  }
+  return r;
+}
+
+__device__ inline Nf4Lut load_nf4_lut(const uint16_t* codebook) {
+  Nf4Lut L;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t v = codebook[4 * w + b];
+      lo |= (v & 0xFFu) << (8 * b);
+      hi |= (v >> 8) << (8 * b);
+    }
+    L.lo[w] = lo;
+    L.hi[w] = hi;
+  }
+  return L;
+}
+
+// ---------------------------------------------------------------------------------------
+// MFMA wrappers (gfx950): D(16x16, fp32) += A(16x32) * B(32x16).
+// Lane l: A row l%16, k = 8*(l/16)+i; B column l%16, same k; D column l%16, rows
+// 4*(l/16)+r, r = 0..3.
+// ---------------------------------------------------------------------------------------
+__device__ inline f4_t mfma16(h8_t a, h8_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline f4_t mfma16(b8_t a, b8_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> output element
+__device__ inline void store_out(void* out, size_t idx, float v, int out_dtype) {
+  if (out_dtype == 2) {
+    static_cast<float*>(out)[idx] = v;
+  } else if (out_dtype == 0) {
+    static_cast<_Float16*>(out)[idx] = (_Float16)v;
+  } else {
+    static_cast<__bf16*>(out)[idx] = (__bf16)v;
+  }
+}
+
+}  // namespace w4a16

@@ -1,0 +1,11 @@
+// w4a16_tiled.hip - batched / prefill W4A16 GEMM (M > 64), LDS-staged MFMA tiles.
+#include "w4a16_device.hpp"
+#include "w4a16_launch.hpp"
+
+namespace w4a16 {
+
+bool tiled_supported(const GemmArgs&) { return false; }
+const char* tiled_name(int, int, int) { return "w4a16_tiled_unavailable"; }
+hipError_t launch_tiled(const GemmArgs&) { return hipErrorNotSupported; }
+
+}  // namespace w4a16
