@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 fused dequantize-GEMM on one MI355X.
+
+One step = every linear of a decode step of the chosen workload, each a W4A16 GEMM through
+the library's C ABI (default: the Llama-3-8B-shaped decode linears, 32 layers x {qkv, o,
+gate+up, down}, M = 1, asymmetric INT4 g128, fp16). Each linear has its own weight buffers,
+so the 3.6 GB set streams from HBM every step (it does not fit the 256 MB Infinity Cache).
+The step is captured once as a HIP graph and replayed; W untimed replays, then K timed
+replays bracketed by synchronisation. Inputs are synthetic (seeded) and already resident
+in HBM when the timed region starts.
+
+Prints one JSON line: metric/value (whole-step effective GB/s over algorithmic bytes),
+a roofline object for the dominant kernel and the CPU oracle's time on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMM effective HBM GB/s at M=1 (% of peak) and TFLOPS at M=256"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+
+WORKLOADS = {
+    # name: shapes (K, N), layers, group size, symmetric, activation dtype, seed config
+    "llama3-8b-decode": dict(shapes=[(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096)],
+                             names=["qkv", "o", "gate_up", "down"], layers=32, g=128,
+                             sym=False, act="f16", config=2, m=1),
+    "llama3-70b-decode": dict(shapes=[(8192, 10240), (8192, 8192), (8192, 57344), (28672, 8192)],
+                              names=["qkv", "o", "gate_up", "down"], layers=80, g=128,
+                              sym=True, act="f16", config=3, m=1),
+    "gemv-4096x4096": dict(shapes=[(4096, 4096)], names=["w"], layers=120, g=128, sym=False,
+                           act="f16", config=1, m=1),
+    "crossover-4096x14336-g128": dict(shapes=[(4096, 14336)], names=["w"], layers=32, g=128,
+                                      sym=False, act="f16", config=4, m=256),
+    "crossover-4096x14336-g32": dict(shapes=[(4096, 14336)], names=["w"], layers=32, g=32,
+                                     sym=False, act="f16", config=4, m=256),
+    "crossover-4096x14336-nf4": dict(shapes=[(4096, 14336)], names=["w"], layers=32, g=64,
+                                     sym=True, act="f16", config=4, m=256, nf4=True),
+    "prefill-2048x8192x28672-bf16": dict(shapes=[(8192, 28672)], names=["w"], layers=4, g=128,
+                                         sym=False, act="bf16", config=5, m=2048),
+}
+
+
+def algo_bytes(M, K, N, g, zeros, nf4=False, act_bytes=2, out_bytes=2):
+    """Bytes the GEMM must move: codes, scales (or NF4 absmax), zeros, x and y."""
+    G = K // g
+    b = K * N // 2 + G * N * 2 + act_bytes * M * K + out_bytes * M * N
+    if zeros and not nf4:
+        b += G * N // 2
+    return b
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_only_int4_w4a16_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, m: int):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they were taken on
+    the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    key = f"{workload}:M={m}"
+    rec = data.get(key)
+    if not rec or rec.get("source_hash") != source_hash() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def build_workload(spec, M, torch, w4, synth):
+    """Device buffers for every (layer, linear): packed codes, scales, zeros; x and y."""
+    act = spec["act"]
+    tdt = torch.float16 if act == "f16" else torch.bfloat16
+    nf4 = spec.get("nf4", False)
+    dev = torch.device("cuda:0")
+    layers = []
+    for layer in range(spec["layers"]):
+        lin = []
+        for si, (K, N) in enumerate(spec["shapes"]):
+            seed = synth.seed_for(spec["config"], si, 0, layer)
+            qw, sc, qz = synth.timing_weights(K, N, spec["g"], seed, symmetric=spec["sym"],
+                                              scale_dtype=act if not nf4 else "f16")
+            qwt = torch.from_numpy(qw).to(dev)
+            packed = w4.pack(qwt)
+            del qwt
+            if act == "bf16" and not nf4:
+                sct = torch.from_numpy(sc.view("int16")).to(dev).view(torch.bfloat16)
+            else:
+                sct = torch.from_numpy(sc).to(dev)
+            qzt = None if qz is None else torch.from_numpy(qz).to(dev)
+            lin.append(dict(K=K, N=N, packed=packed, scales=sct, qzeros=qzt))
+        layers.append(lin)
+    xs, ys = [], []
+    for si, (K, N) in enumerate(spec["shapes"]):
+        x = synth.activations(M, K, synth.seed_for(spec["config"], si, synth.ROLE_X), act)
+        xt = torch.from_numpy(x.view("int16") if act == "bf16" else x).to(dev)
+        if act == "bf16":
+            xt = xt.view(torch.bfloat16)
+        xs.append(xt)
+        ys.append(torch.empty((M, N), dtype=tdt, device=dev))
+    codebook = None
+    if nf4:
+        import numpy as np
+        vals = np.loadtxt(os.path.join(ROOT, "tests", "golden", "nf4_codebook.txt"))
+        codebook = torch.from_numpy(vals.astype(np.float16)).to(dev)
+    torch.cuda.synchronize()
+    return layers, xs, ys, codebook
+
+
+def make_step(spec, layers, xs, ys, codebook, w4):
+    g = spec["g"]
+    nf4 = spec.get("nf4", False)
+
+    def step():
+        for lin in layers:
+            for si, L in enumerate(lin):
+                if nf4:
+                    w4.gemm_nf4(xs[si], L["packed"], L["scales"], codebook, g, out=ys[si])
+                else:
+                    w4.gemm(xs[si], L["packed"], L["scales"], L["qzeros"], g, out=ys[si])
+    return step
+
+
+def cpu_baseline(spec, M, budget_s=20.0):
+    """Time the CPU oracle (dequantize + fp64 matmul, as written) on layer 0's linears,
+    stopping once ``budget_s`` of CPU time has been spent (at least one linear)."""
+    import numpy as np
+
+    import oracle
+    from weight_only_int4_w4a16_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    act = spec["act"]
+    nf4 = spec.get("nf4", False)
+    done_bytes, done_s, names = 0, 0.0, []
+    for si, (K, N) in enumerate(spec["shapes"]):
+        seed = synth.seed_for(spec["config"], si, 0, 0)
+        qw, sc, qz = synth.timing_weights(K, N, spec["g"], seed, symmetric=spec["sym"],
+                                          scale_dtype=act if not nf4 else "f16")
+        x = synth.activations(M, K, synth.seed_for(spec["config"], si, synth.ROLE_X), act)
+        t0 = time.perf_counter()
+        if nf4:
+            w_hat = oracle.dequant_nf4(qw, sc, oracle.nf4_codebook(), spec["g"], act)
+        else:
+            w_hat = oracle.dequant_affine(qw, sc, qz, spec["g"], act)
+        oracle.gemm_ref(x, w_hat, act)
+        dt = time.perf_counter() - t0
+        done_s += dt
+        done_bytes += algo_bytes(M, K, N, spec["g"], qz is not None, nf4)
+        names.append(spec["names"][si])
+        del w_hat
+        if done_s >= budget_s:
+            break
+    return {"value": round(done_bytes / done_s / 1e9, 4), "unit": "GB/s",
+            "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"layer 0 linears {'+'.join(names)} of {spec['name']} at M={M}, "
+                       f"one pass each ({done_s:.1f} s); NumPy dequant on 1 thread, "
+                       f"fp64 matmul on {blas_threads} BLAS threads")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3-8b-decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--m", type=int, default=None, help="rows of x (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a HIP graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the sharding plan is described in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import weight_only_int4_w4a16_amd as w4
+    from weight_only_int4_w4a16_amd import synth
+
+    spec = dict(WORKLOADS[args.workload])
+    spec["name"] = args.workload
+    M = spec["m"] if args.m is None else args.m
+    nf4 = spec.get("nf4", False)
+    layers, xs, ys, codebook = build_workload(spec, M, torch, w4, synth)
+    step = make_step(spec, layers, xs, ys, codebook, w4)
+
+    launches = [(K, N) for _ in range(spec["layers"]) for (K, N) in spec["shapes"]]
+    zeros = not spec["sym"]
+    step_bytes = sum(algo_bytes(M, K, N, spec["g"], zeros, nf4) for K, N in launches)
+    step_flops = sum(2 * M * N * K for K, N in launches)
+    kernel = w4.kernel_name(M, spec["shapes"][0][0], spec["shapes"][0][1], spec["g"])
+
+    # warm-up eagerly once (also checks every call succeeds), then capture the step
+    step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        run()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+
+    # the step is made of this one kernel only: its average launch duration is the event
+    # time of the timed region over the number of launches (dispatch gaps included)
+    n_launch = len(launches) * args.steps
+    avg_launch_us = gpu_ms * 1e3 / n_launch
+    bytes_per_launch = step_bytes / len(launches)
+    flops_per_launch = step_flops / len(launches)
+    mem_bound = M <= 64
+    if mem_bound:
+        achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = flops_per_launch / (avg_launch_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = load_traffic(kernel, args.workload, M)
+    roof["kernel"] = kernel
+    roof["avg_launch_us"] = round(avg_launch_us, 3)
+    roof["algo_bytes_per_launch"] = int(bytes_per_launch)
+
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    tflops = step_flops / (ms_per_step * 1e-3) / 1e12
+    if mem_bound:
+        value, unit = gbs, "GB/s"
+    else:
+        value, unit = tflops, "TFLOP/s"
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec["act"], "data": "synthetic (seeded random INT4 codes and scales; "
+                                      "activations ~N(0,1))",
+        "config": {"workload": args.workload, "M": M, "shapes_KxN": spec["shapes"],
+                   "layers": spec["layers"], "group_size": spec["g"],
+                   "format": "nf4" if nf4 else ("sym" if spec["sym"] else "asym"),
+                   "launches_per_step": len(launches), "graph": graph is not None,
+                   "weight_set_GB": round(step_bytes / 1e9, 3)},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tflops": round(tflops, 2),
+        "wall_s": round(wall_s, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, M)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

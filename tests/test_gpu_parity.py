@@ -215,3 +215,38 @@ def test_full_size_sampled_strips(M, K, N, g, act, fmt):
     assert_close(y[:, cols], y_ref, "fp32 out, sampled strips")
     del d
     torch.cuda.empty_cache()
+
+
+def test_graph_replays_match_eager():
+    """The benchmark replays a captured HIP graph of GEMM launches: every replay, with eager
+    work and synchronisation between replays, must equal the eager result bit for bit."""
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    cases = [rtn_case(1, 1024, 256, 128, seed=11), rtn_case(4, 512, 128, 32, seed=12)]
+    devs = [device_inputs(c) for c in cases]
+    outs = [torch.empty((c["M"], c["N"]), dtype=torch.float16, device="cuda") for c in cases]
+
+    def step():
+        for c, d, o in zip(cases, devs, outs):
+            w4.gemm(d["x"], d["packed"], d["scales"], d["qzeros"], c["g"], out=o)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [from_dev(o).copy() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for o in outs:
+            o.fill_(0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert np.array_equal(from_dev(o).view(np.uint16), e.view(np.uint16)), f"replay {r}"
