@@ -29,7 +29,8 @@
  *     nothing is launched in either case. A failed launch returns W4A16_ERR_HIP.
  *     Faults during execution surface at the caller's next synchronization.
  *   - There is no slow or CPU fallback path.
- *   - No global mutable state: calls on different streams may run concurrently.
+ *   - The only global state is a per-device cache of the compute-unit count. Calls on
+ *     different streams may run concurrently if they use distinct workspaces.
  *
  * Supported shapes: K % 32 == 0, K % group_size == 0, N % 16 == 0, M >= 0, K, N > 0,
  * group_size in {32, 64, 128}; K * N < 2^34 (packed weight below 8 GiB).
@@ -50,7 +51,8 @@ typedef enum {
   W4A16_OK = 0,
   W4A16_ERR_ARG = 1,          /* null pointer, misalignment, inconsistent shape or dtype */
   W4A16_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (e.g. N % 16 != 0)    */
-  W4A16_ERR_HIP = 3           /* the HIP runtime rejected a launch                       */
+  W4A16_ERR_HIP = 3,          /* the HIP runtime rejected a launch                       */
+  W4A16_ERR_WORKSPACE = 4     /* workspace missing, misaligned or smaller than required  */
 } w4a16_status;
 
 /* Bytes of the device-layout weight for a K x N matrix: K_pad * N / 2 with
@@ -66,16 +68,27 @@ size_t w4a16_packed_bytes(int K, int N);
  * Must not alias qweight. */
 w4a16_status w4a16_pack(const int32_t* qweight, int K, int N, int32_t* packed, void* stream);
 
+/* Bytes of scratch device memory w4a16_gemm / w4a16_gemm_nf4 need for this shape on the
+ * current device (partial sums of K-slices and one counter per 16-column strip). The
+ * caller allocates it, zero-fills it ONCE before its first use, and may then reuse it for
+ * any number of calls: every call leaves it zero-filled again. Calls that may run
+ * concurrently (different streams) need distinct workspaces. Returns 0 for bad shapes. */
+size_t w4a16_workspace_bytes(int M, int K, int N, int group_size);
+
 /* The W4A16 GEMM with affine (asymmetric) or symmetric INT4 weights.
  *   x         [in]  act [M][K], act = W4A16_F16 or W4A16_BF16
  *   packed    [in]  output of w4a16_pack for this K, N
  *   scales    [in]  act [K/group_size][N]
  *   qzeros    [in]  int32 [K/group_size][N/8], or NULL for symmetric codes (zero 8)
  *   out       [out] out_dtype [M][N], out_dtype = act or W4A16_F32
- * M = 0 is a no-op. Results are deterministic (no atomics in the reduction). */
+ *   workspace [in/out] >= w4a16_workspace_bytes(M, K, N, group_size) bytes, 256-byte
+ *                   aligned, zero-filled before first use (see above)
+ * M = 0 is a no-op. Results are deterministic: partial sums are combined in a fixed
+ * order, never with floating-point atomics. */
 w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
                         const int32_t* packed, const void* scales, const int32_t* qzeros,
-                        int group_size, void* out, w4a16_dtype out_dtype, void* stream);
+                        int group_size, void* out, w4a16_dtype out_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* The W4A16 GEMM with NF4 weights ("INT4 and Low-Bit Inference", section 5, The formats;
  * "INT4", section INT4, FP4, and NF4 are not identical).
@@ -86,7 +99,8 @@ w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
 w4a16_status w4a16_gemm_nf4(const void* x, int M, int K, int N, w4a16_dtype act,
                             const int32_t* packed, const uint16_t* absmax,
                             const uint16_t* codebook, int block_size, void* out,
-                            w4a16_dtype out_dtype, void* stream);
+                            w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Test hook: write W_hat[K][N] (row-major, in `wdtype` = F16 or BF16) using the same
  * device dequantization routine the GEMM kernels use. scales are in wdtype. */

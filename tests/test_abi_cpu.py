@@ -25,7 +25,7 @@ def L():
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for n in ("w4a16_pack", "w4a16_gemm", "w4a16_gemm_nf4", "w4a16_dequant",
-              "w4a16_dequant_nf4", "w4a16_packed_bytes", "w4a16_kernel_name",
+              "w4a16_dequant_nf4", "w4a16_packed_bytes", "w4a16_workspace_bytes", "w4a16_kernel_name",
               "w4a16_status_string", "w4a16_version"):
         assert n in names
 
@@ -44,12 +44,12 @@ def test_packed_bytes(L):
     assert packed_bytes(8192, 57344) == 8192 * 57344 // 2
 
 
-def _gemm(L, x=1, M=1, K=4096, N=4096, act=0, packed=16, scales=16, qzeros=16, g=128,
-          out=16, odt=0):
+def _gemm(L, x=16, M=1, K=4096, N=4096, act=0, packed=16, scales=16, qzeros=16, g=128,
+          out=16, odt=0, ws=256, wsb=1 << 30):
     vp = ctypes.c_void_p
     return L.w4a16_gemm(vp(x) if x else None, M, K, N, act, vp(packed) if packed else None,
                         vp(scales) if scales else None, vp(qzeros) if qzeros else None, g,
-                        vp(out) if out else None, odt, None)
+                        vp(out) if out else None, odt, vp(ws) if ws else None, wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -74,12 +74,21 @@ def test_gemm_rejects_bad_arguments_before_launch(L, kw, status):
 
 
 def test_gemm_m0_is_a_noop(L):
-    assert _gemm(L, M=0, x=0, packed=0, scales=0, out=0) == 0
+    assert _gemm(L, M=0, x=0, packed=0, scales=0, out=0, ws=0, wsb=0) == 0
+
+
+def test_workspace_bytes(L):
+    from weight_only_int4_w4a16_amd import workspace_bytes
+    assert workspace_bytes(0, 4096, 4096, 128) == 0
+    assert workspace_bytes(1, 4096, 4096, 100) == 0
+    for M, K, N in ((1, 4096, 4096), (16, 14336, 4096), (64, 4096, 28672), (1, 352, 48)):
+        assert workspace_bytes(M, K, N, 32) == 0    # the decode kernels reduce in LDS
 
 
 def test_nf4_requires_codebook(L):
     vp = ctypes.c_void_p
-    st = L.w4a16_gemm_nf4(vp(16), 1, 4096, 4096, 0, vp(16), vp(16), None, 64, vp(16), 0, None)
+    st = L.w4a16_gemm_nf4(vp(16), 1, 4096, 4096, 0, vp(16), vp(16), None, 64, vp(16), 0,
+                          vp(256), 1 << 30, None)
     assert st == 1
 
 
@@ -95,9 +104,9 @@ def test_pack_and_dequant_reject_bad_arguments(L):
 
 def test_kernel_name_and_strings(L):
     from weight_only_int4_w4a16_amd import kernel_name, version
-    assert kernel_name(1, 4096, 4096, 128).startswith("w4a16_skinny")
+    assert kernel_name(1, 4096, 4096, 128).startswith("w4a16_decode")
     assert kernel_name(0, 4096, 4096, 128) == "none"
-    for s in range(4):
+    for s in range(5):
         assert L.w4a16_status_string(s)
     assert version()
 

@@ -14,9 +14,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 F16, BF16, F32 = 0, 1, 2
-OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 
 _lib = None
+_workspaces = {}   # device index -> zero-filled uint8 tensor
 
 
 class W4A16Error(RuntimeError):
@@ -39,9 +40,11 @@ def lib() -> ctypes.CDLL:
     L.w4a16_packed_bytes.restype = sz
     L.w4a16_pack.argtypes = [vp, i32, i32, vp, vp]
     L.w4a16_pack.restype = i32
-    L.w4a16_gemm.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp]
+    L.w4a16_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.w4a16_workspace_bytes.restype = sz
+    L.w4a16_gemm.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
     L.w4a16_gemm.restype = i32
-    L.w4a16_gemm_nf4.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp]
+    L.w4a16_gemm_nf4.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
     L.w4a16_gemm_nf4.restype = i32
     L.w4a16_dequant.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
     L.w4a16_dequant.restype = i32
@@ -93,6 +96,34 @@ def packed_bytes(K: int, N: int) -> int:
     return int(lib().w4a16_packed_bytes(K, N))
 
 
+def workspace_bytes(M: int, K: int, N: int, group_size: int) -> int:
+    return int(lib().w4a16_workspace_bytes(M, K, N, group_size))
+
+
+def _workspace(device, nbytes: int, workspace=None):
+    """The caller's workspace, or a cached zero-filled buffer for the device.
+
+    The library leaves a workspace zero-filled after every call, so one buffer serves all
+    calls that do not run concurrently; callers that launch GEMMs on several streams at
+    once pass their own ``workspace`` per stream. It is never allocated while a HIP graph
+    is being captured (warm up eagerly first).
+    """
+    torch = _torch()
+    if workspace is not None:
+        return workspace
+    if nbytes == 0:
+        return None
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise W4A16Error("workspace must be allocated before graph capture: run the same "
+                             "calls once eagerly on this stream first", ERR_WORKSPACE)
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
 def pack(qweight):
     """Canonical ``qweight[K/8, N]`` int32 -> the library's device layout (int32 tensor)."""
     torch = _torch()
@@ -107,10 +138,11 @@ def pack(qweight):
     return out
 
 
-def gemm(x, packed, scales, qzeros, group_size: int, out_dtype=None, out=None):
+def gemm(x, packed, scales, qzeros, group_size: int, out_dtype=None, out=None, workspace=None):
     """``y = x @ W_hat`` with affine (``qzeros`` given) or symmetric (``qzeros=None``) INT4.
 
     ``x[M, K]`` fp16/bf16, ``scales[K/g, N]`` in x's dtype, ``qzeros[K/g, N/8]`` int32.
+    ``workspace``: optional zero-filled uint8 device tensor (see ``workspace_bytes``).
     """
     torch = _torch()
     M, K = x.shape
@@ -120,13 +152,16 @@ def gemm(x, packed, scales, qzeros, group_size: int, out_dtype=None, out=None):
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
     if scales.dtype != x.dtype:
         raise W4A16Error("scales must have the activation dtype")
+    ws = _workspace(x.device, workspace_bytes(M, K, N, group_size) if M else 0, workspace)
     st = lib().w4a16_gemm(_ptr(x), M, K, N, _dt(x.dtype), _ptr(packed), _ptr(scales),
-                          _ptr(qzeros), group_size, _ptr(out), _dt(out.dtype), _stream(x))
+                          _ptr(qzeros), group_size, _ptr(out), _dt(out.dtype), _ptr(ws),
+                          0 if ws is None else ws.numel() * ws.element_size(), _stream(x))
     _check(st, "w4a16_gemm")
     return out
 
 
-def gemm_nf4(x, packed, absmax, codebook, block_size: int = 64, out_dtype=None, out=None):
+def gemm_nf4(x, packed, absmax, codebook, block_size: int = 64, out_dtype=None, out=None,
+             workspace=None):
     """``y = x @ W_hat`` with NF4 weights: fp16 ``absmax[K/b, N]``, fp16 ``codebook[16]``."""
     torch = _torch()
     M, K = x.shape
@@ -136,8 +171,10 @@ def gemm_nf4(x, packed, absmax, codebook, block_size: int = 64, out_dtype=None, 
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
     if absmax.dtype != torch.float16 or codebook.dtype != torch.float16:
         raise W4A16Error("NF4 absmax and codebook are fp16")
+    ws = _workspace(x.device, workspace_bytes(M, K, N, block_size) if M else 0, workspace)
     st = lib().w4a16_gemm_nf4(_ptr(x), M, K, N, _dt(x.dtype), _ptr(packed), _ptr(absmax),
-                              _ptr(codebook), block_size, _ptr(out), _dt(out.dtype), _stream(x))
+                              _ptr(codebook), block_size, _ptr(out), _dt(out.dtype), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(), _stream(x))
     _check(st, "w4a16_gemm_nf4")
     return out
 

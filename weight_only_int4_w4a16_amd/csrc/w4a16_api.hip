@@ -1,5 +1,5 @@
 // w4a16_api.hip - the C ABI declared in include/w4a16.h: host-side argument checks, then
-// dispatch on M to the decode (skinny) or batched (tiled) kernels. Nothing is launched
+// dispatch on M to the decode or batched (tiled) kernels. Nothing is launched
 // unless every check passes; there is no fallback path.
 #include "w4a16.h"
 #include "w4a16_launch.hpp"
@@ -24,6 +24,15 @@ w4a16_status check_shape(int K, int N, int gs) {
 
 w4a16_status from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
+bool use_tiled(const GemmArgs& a) { return a.M > 64 && w4a16::tiled_supported(a); }
+
+size_t workspace_need(int M, int K, int N, int gs) {
+  GemmArgs a{};
+  a.M = M; a.K = K; a.N = N; a.group_size = gs;
+  if (use_tiled(a)) return w4a16::tiled_workspace_bytes(M, K, N);
+  return w4a16::decode_config(M < 64 ? M : 64, K, N, gs, w4a16::ACT_F16).workspace_bytes;
+}
+
 w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
   if (a.M < 0) return W4A16_ERR_ARG;
   w4a16_status st = check_shape(a.K, a.N, a.group_size);
@@ -38,8 +47,11 @@ w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
   if (a.codebook && !aligned(a.codebook, 2)) return W4A16_ERR_ARG;
   a.act = act == W4A16_F16 ? w4a16::ACT_F16 : w4a16::ACT_BF16;
   a.out_dtype = (int)out_dtype;
-  if (a.M > 64 && w4a16::tiled_supported(a)) return from_hip(w4a16::launch_tiled(a));
-  return from_hip(w4a16::launch_skinny(a));
+  const size_t need = workspace_need(a.M, a.K, a.N, a.group_size);
+  if (need && (!a.workspace || !aligned(a.workspace, 256) || a.workspace_bytes < need))
+    return W4A16_ERR_WORKSPACE;
+  if (use_tiled(a)) return from_hip(w4a16::launch_tiled(a));
+  return from_hip(w4a16::launch_decode(a));
 }
 
 }  // namespace
@@ -61,9 +73,16 @@ w4a16_status w4a16_pack(const int32_t* qweight, int K, int N, int32_t* packed, v
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t w4a16_workspace_bytes(int M, int K, int N, int group_size) {
+  if (M < 0 || check_shape(K, N, group_size) != W4A16_OK) return 0;
+  if (M == 0) return 0;
+  return workspace_need(M, K, N, group_size);
+}
+
 w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
                         const int32_t* packed, const void* scales, const int32_t* qzeros,
-                        int group_size, void* out, w4a16_dtype out_dtype, void* stream) {
+                        int group_size, void* out, w4a16_dtype out_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   GemmArgs a{};
   a.x = x; a.M = M; a.K = K; a.N = N;
   a.packed = reinterpret_cast<const uint32_t*>(packed);
@@ -72,6 +91,7 @@ w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
   a.codebook = nullptr; a.nf4 = false;
   a.group_size = group_size;
   a.out = out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   a.stream = static_cast<hipStream_t>(stream);
   return gemm_common(a, act, out_dtype);
 }
@@ -79,7 +99,8 @@ w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
 w4a16_status w4a16_gemm_nf4(const void* x, int M, int K, int N, w4a16_dtype act,
                             const int32_t* packed, const uint16_t* absmax,
                             const uint16_t* codebook, int block_size, void* out,
-                            w4a16_dtype out_dtype, void* stream) {
+                            w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   GemmArgs a{};
   a.x = x; a.M = M; a.K = K; a.N = N;
   a.packed = reinterpret_cast<const uint32_t*>(packed);
@@ -88,6 +109,7 @@ w4a16_status w4a16_gemm_nf4(const void* x, int M, int K, int N, w4a16_dtype act,
   a.codebook = codebook; a.nf4 = true;
   a.group_size = block_size;
   a.out = out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   a.stream = static_cast<hipStream_t>(stream);
   return gemm_common(a, act, out_dtype);
 }
@@ -137,8 +159,8 @@ const char* w4a16_kernel_name(int M, int K, int N, int group_size) {
   if (M <= 0) return "none";
   GemmArgs a{};
   a.M = M; a.K = K; a.N = N; a.group_size = group_size;
-  if (M > 64 && w4a16::tiled_supported(a)) return w4a16::tiled_name(M, K, N);
-  return w4a16::skinny_name(M);
+  if (use_tiled(a)) return w4a16::tiled_name(M, K, N);
+  return w4a16::decode_name(M < 64 ? M : 64, K, N, group_size, w4a16::ACT_F16);
 }
 
 const char* w4a16_status_string(w4a16_status s) {
@@ -147,6 +169,7 @@ const char* w4a16_status_string(w4a16_status s) {
     case W4A16_ERR_ARG: return "invalid argument";
     case W4A16_ERR_UNSUPPORTED: return "unsupported shape";
     case W4A16_ERR_HIP: return "HIP launch failed";
+    case W4A16_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
   }
   return "unknown status";
 }

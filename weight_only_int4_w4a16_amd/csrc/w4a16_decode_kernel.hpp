@@ -1,0 +1,294 @@
+// w4a16_decode_kernel.hpp - memory-bound W4A16 GEMM for small M (decode): up to 64 rows per launch.
+//
+// "INT8 vs INT4 Quantization, in depth", section "Two regimes": at small batch a linear
+// layer waits on weight bytes, so this kernel's job is to stream the packed codes once at
+// full HBM rate and hide unpacking, dequantization and the MFMAs under the loads.
+//
+// Work split. A workgroup owns a tile of SW adjacent 16-column strips over the whole K
+// range; its W waves split the k-blocks of the tile into W contiguous slices, so every
+// wave streams SW independent runs of 1 KiB blocks (the packed layout stores each strip's
+// k-blocks contiguously). No wave ever waits for another until the very end, where the W
+// partial tiles are summed through LDS in wave order (deterministic, no atomics, no global
+// scratch). Workgroups are numbered so that neighbouring tiles, which share the cache lines
+// of their scales and zero-points, run on the same XCD (dispatch is round-robin over the
+// eight XCDs, each with its own L2).
+//
+// Pipeline. A wave moves its slice in groups of D k-blocks x SW strips (4 blocks, i.e.
+// 4 KiB) with two register sets: group t+1 is in flight while group t is dequantized and
+// multiplied, and every group's loads are issued together, so the in-order load counter
+// never makes one set wait for the other.
+//
+// Activations. When x fits, each wave copies the k-slice of x it needs into its own LDS
+// region (no barrier) and reads the MFMA A fragments from there; one fragment serves all
+// SW strips. Otherwise the fragments are loaded with the codes of their k-block (D = 1).
+// Rows of the 16-row MFMA tile past M repeat row M-1 and are never stored (an output row
+// depends on its own A row only).
+#pragma once
+
+#include <type_traits>
+
+#include "w4a16_device.hpp"
+#include "w4a16_launch.hpp"
+
+namespace w4a16 {
+
+enum Fmt { FMT_ASYM = 0, FMT_SYM = 1, FMT_NF4 = 2 };
+
+template <int ACT>
+struct ActT;
+template <>
+struct ActT<ACT_F16> { typedef h8_t type; };
+template <>
+struct ActT<ACT_BF16> { typedef b8_t type; };
+
+struct DecodeParams {
+  const uint16_t* x;
+  int M, K, N;
+  const u4_t* packed;
+  const uint16_t* scales;   // act [K/gs][N], or fp16 NF4 absmax
+  const uint32_t* qzeros;   // FMT_ASYM only
+  const uint16_t* codebook; // FMT_NF4 only
+  void* out;
+  int out_dtype;
+  int KC;        // k-blocks per strip
+  int NG;        // scale groups along K (K / group size)
+  int W;         // waves per workgroup
+  int slice;     // k-blocks per wave (the last waves may get fewer or none)
+  int tiles;     // workgroups (= strips / SW)
+  int xstride;   // LDS row stride of x in halves (XL)
+  int xslice;    // LDS halves reserved per wave for its slice of x (XL)
+  int GPC;       // scale groups per 128-k block (128 / group size)
+};
+
+// workgroup -> tile: tiles [start(x), start(x) + count(x)) run on XCD x = blockIdx % 8
+__device__ __forceinline__ int tile_of(int b, int G) {
+  const int q = G >> 3, r = G & 7, x = b & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
+template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, int LB>
+__global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
+  typedef typename ActT<ACT>::type AT;
+  constexpr int D = XL ? 4 / SW : 1;  // k-blocks per group
+  constexpr int SPG = 4 / GPC;        // 32-k steps per scale group
+  constexpr bool ZEROS = FMT == FMT_ASYM;
+
+  extern __shared__ uint32_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile = tile_of(blockIdx.x, p.tiles);
+  const int K = p.K, N = p.N, KC = p.KC, rows = p.M;
+  const int kc0 = min(wave * p.slice, KC);
+  const int kc1 = min(kc0 + p.slice, KC);
+  const int ng = (kc1 - kc0 + D - 1) / D;  // groups of this wave
+  const int col = tile * SW * 16 + (lane & 15);  // this lane's column in strip 0 of the tile
+  const int shift = 4 * (lane & 7);              // nibble of the column in its zero word
+
+  float* red = reinterpret_cast<float*>(lds);                                   // [W][SW][rows][16]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(red + (size_t)p.W * SW * rows * 16) +
+                 (size_t)wave * p.xslice;                                        // [rows][xstride]
+
+  // ---- group loads: codes, per-group metadata and (not XL) the A fragments ----
+  u4_t bA[D][SW], bB[D][SW];
+  uint16_t sA[D][SW][GPC], sB[D][SW][GPC];
+  uint32_t zA[D][SW][GPC], zB[D][SW][GPC];
+  u4_t xA[XL ? 1 : MT][4], xB[XL ? 1 : MT][4];
+
+  auto load_group = [&](u4_t(&b)[D][SW], uint16_t(&s)[D][SW][GPC], uint32_t(&z)[D][SW][GPC],
+                        u4_t(&xf)[XL ? 1 : MT][4], int t) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int kc = min(kc0 + t * D + d, kc1 - 1);  // past the slice: reload its last block
+#pragma unroll
+      for (int sw = 0; sw < SW; ++sw) {
+        const int nt = tile * SW + sw;
+        b[d][sw] = __builtin_nontemporal_load(p.packed + ((size_t)nt * KC + kc) * 64 + lane);
+#pragma unroll
+        for (int gi = 0; gi < GPC; ++gi) {
+          const int g = min(kc * GPC + gi, p.NG - 1);  // groups past K are never used
+          s[d][sw][gi] = p.scales[(size_t)g * N + col + sw * 16];
+          if constexpr (ZEROS) z[d][sw][gi] = p.qzeros[(size_t)g * (N >> 3) + ((col + sw * 16) >> 3)];
+        }
+      }
+      if constexpr (!XL) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = min(mt * 16 + (lane & 15), rows - 1);
+          const uint16_t* xr = p.x + (size_t)m * K + (size_t)kc * 128 + (lane >> 4) * 8;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kj = kc * 128 + j * 32 < K ? j * 32 : 0;  // ragged tail: unused, in bounds
+            xf[mt][j] = *reinterpret_cast<const u4_t*>(xr + kj);
+          }
+        }
+      }
+    }
+  };
+
+  f4_t acc[SW][MT];
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[sw][mt] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  Nf4Lut lut;
+  if constexpr (FMT == FMT_NF4) lut = load_nf4_lut(p.codebook);
+
+  // GUARD: the group may run past the wave's slice or end inside a ragged last k-block;
+  // full groups take the branch-free copy
+  auto compute_group = [&](const u4_t(&b)[D][SW], const uint16_t(&s)[D][SW][GPC],
+                           const uint32_t(&z)[D][SW][GPC], const u4_t(&xf)[XL ? 1 : MT][4],
+                           int t, auto guard) {
+    constexpr bool GUARD = decltype(guard)::value;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int kc = kc0 + t * D + d;
+      if (!GUARD || kc < kc1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!GUARD || kc * 128 + j * 32 < K) {
+            AT a[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              u4_t v;
+              if constexpr (XL) {
+                const int m = min(mt * 16 + (lane & 15), rows - 1);
+                v = *reinterpret_cast<const u4_t*>(xs + (size_t)m * p.xstride +
+                                                   (kc - kc0) * 128 + j * 32 + (lane >> 4) * 8);
+              } else {
+                v = xf[mt][j];
+              }
+              a[mt] = __builtin_bit_cast(AT, v);
+            }
+            const int gi = j / SPG;
+#pragma unroll
+            for (int sw = 0; sw < SW; ++sw) {
+              const uint32_t w = b[d][sw][j];
+              const uint32_t sraw = s[d][sw][gi];
+              AT bf;
+              if constexpr (FMT == FMT_NF4) {
+                if constexpr (ACT == ACT_F16)
+                  bf = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
+                else
+                  bf = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
+              } else {
+                const uint32_t zq = ZEROS ? (z[d][sw][gi] >> shift) & 0xFu : 8u;
+                if constexpr (ACT == ACT_F16)
+                  bf = dequant_word_f16(w, make_zero_f16(zq), as_h2(sraw * 0x00010001u));
+                else
+                  bf = dequant_word_bf16(w, make_zero_f32(zq, __builtin_bit_cast(float, sraw << 16)));
+              }
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) acc[sw][mt] = mfma16(a[mt], bf, acc[sw][mt]);
+            }
+          }
+        }
+      }
+    }
+  };
+  // a group is full when all its k-blocks lie in the slice and hold four 32-k steps
+  const int kfull = K >> 7;  // k-blocks without a ragged tail
+  const int kend = kc1 < kfull ? kc1 : kfull;
+  auto compute = [&](const u4_t(&b)[D][SW], const uint16_t(&s)[D][SW][GPC],
+                     const uint32_t(&z)[D][SW][GPC], const u4_t(&xf)[XL ? 1 : MT][4], int t) {
+    if (kc0 + (t + 1) * D <= kend) compute_group(b, s, z, xf, t, std::false_type{});
+    else compute_group(b, s, z, xf, t, std::true_type{});
+  };
+
+  if (ng > 0) {
+    load_group(bA, sA, zA, xA, 0);
+    if constexpr (XL) {
+      // this wave's k-slice of x -> its LDS region (the first group's loads are already in
+      // flight, so their latency and the copy's overlap)
+      const int kbeg = kc0 * 128;
+      const int chunks = (min(kc1 * 128, K) - kbeg) >> 3;  // 16-byte chunks per row
+      for (int m = 0; m < rows; ++m)
+        for (int c = lane; c < chunks; c += 64)
+          *reinterpret_cast<u4_t*>(xs + (size_t)m * p.xstride + c * 8) =
+              *reinterpret_cast<const u4_t*>(p.x + (size_t)m * K + kbeg + c * 8);
+    }
+    int t = 0;
+    for (; t + 1 < ng; t += 2) {
+      load_group(bB, sB, zB, xB, t + 1);
+      compute(bA, sA, zA, xA, t);
+      if (t + 2 < ng) load_group(bA, sA, zA, xA, t + 2);
+      compute(bB, sB, zB, xB, t + 1);
+    }
+    if (t < ng) compute(bA, sA, zA, xA, t);
+  }
+
+  // ---- sum the W partial tiles in wave order ----
+#pragma unroll
+  for (int sw = 0; sw < SW; ++sw)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mt * 16 + 4 * (lane >> 4) + r;
+        if (m < rows) red[(((size_t)wave * SW + sw) * rows + m) * 16 + (lane & 15)] = acc[sw][mt][r];
+      }
+  __syncthreads();
+  const int per_wave = SW * rows * 16;
+  for (int e = threadIdx.x; e < per_wave; e += blockDim.x) {
+    float v = 0.f;
+    for (int w = 0; w < p.W; ++w) v += red[(size_t)w * per_wave + e];
+    const int sw = e / (rows * 16);
+    const int rem = e - sw * rows * 16;
+    const int m = rem >> 4, c = rem & 15;
+    store_out(p.out, (size_t)m * N + (size_t)(tile * SW + sw) * 16 + c, v, p.out_dtype);
+  }
+}
+
+// Launch the instantiation matching the configuration (defined once per activation type and
+// weight format, in the w4a16_decode_<act>_<fmt>.hip units).
+template <int ACT, int FMT>
+hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s);
+
+constexpr int kMaxWavesMt1 = 16;  // waves per workgroup (1024 threads) for one 16-row tile
+constexpr int kMaxWavesMtN = 8;   // more 16-row tiles: more accumulators per lane
+
+template <int ACT, int MT, int SW, int GPC, int FMT, bool XL>
+hipError_t decode_launch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
+  constexpr int LB = MT == 1 ? 64 * kMaxWavesMt1 : 64 * kMaxWavesMtN;
+  hipLaunchKernelGGL((decode_kernel<ACT, MT, SW, GPC, FMT, XL, LB>), dim3(c.tiles), dim3(64 * c.W),
+                     c.lds_bytes, s, p);
+  return hipGetLastError();
+}
+
+// The instantiated set (all free of register spills on gfx950): x in LDS with one 16-row
+// tile: SW 1 or 2, and SW 4 for fp16 with one scale group per k-block; every other case SW 1.
+template <int ACT, int FMT, int MT, bool XL>
+hipError_t decode_dispatch_gpc(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
+  if constexpr (MT == 1 && XL) {
+    if (c.SW == 4) {
+      if constexpr (ACT == ACT_F16)
+        if (p.GPC == 1) return decode_launch<ACT, 1, 4, 1, FMT, true>(p, c, s);
+      return hipErrorNotSupported;
+    }
+    if (c.SW == 2) {
+      switch (p.GPC) {
+        case 1: return decode_launch<ACT, 1, 2, 1, FMT, true>(p, c, s);
+        case 2: return decode_launch<ACT, 1, 2, 2, FMT, true>(p, c, s);
+        default: return decode_launch<ACT, 1, 2, 4, FMT, true>(p, c, s);
+      }
+    }
+  }
+  if (c.SW != 1) return hipErrorNotSupported;
+  switch (p.GPC) {
+    case 1: return decode_launch<ACT, MT, 1, 1, FMT, XL>(p, c, s);
+    case 2: return decode_launch<ACT, MT, 1, 2, FMT, XL>(p, c, s);
+    default: return decode_launch<ACT, MT, 1, 4, FMT, XL>(p, c, s);
+  }
+}
+
+template <int ACT, int FMT>
+hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
+  if (c.MT == 1) return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 1, true>(p, c, s)
+                                   : decode_dispatch_gpc<ACT, FMT, 1, false>(p, c, s);
+  if (c.MT == 2) return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 2, true>(p, c, s)
+                                   : decode_dispatch_gpc<ACT, FMT, 2, false>(p, c, s);
+  return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 4, true>(p, c, s)
+                    : decode_dispatch_gpc<ACT, FMT, 4, false>(p, c, s);
+}
+
+}  // namespace w4a16

@@ -20,16 +20,35 @@ struct GemmArgs {
   int group_size;
   void* out;
   int out_dtype;           // 0 fp16, 1 bf16, 2 fp32
+  void* workspace;         // zero-filled before first use; left zero-filled after each call
+  size_t workspace_bytes;
   hipStream_t stream;
 };
+
+// launch geometry of the decode kernel (at most 64 rows of x per launch)
+struct DecodeConfig {
+  int KC, NT;        // k-blocks per strip, 16-column strips
+  int rows, MT;      // rows of x, 16-row MFMA tiles
+  int SW;            // strips per workgroup tile (1, 2 or 4)
+  int tiles;         // workgroups
+  int W;             // waves per workgroup; wave w streams k-blocks [w*slice, (w+1)*slice)
+  int slice;
+  int xstride;       // LDS row stride of x (halves)
+  int xslice;        // LDS halves per wave for its slice of x
+  bool x_in_lds;     // activations staged in LDS
+  size_t lds_bytes;  // dynamic LDS per workgroup
+  size_t workspace_bytes;
+};
+DecodeConfig decode_config(int M, int K, int N, int group_size, int act);
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 hipError_t launch_pack(const uint32_t* qweight, int K, int N, uint32_t* packed, hipStream_t s);
 hipError_t launch_dequant(const GemmArgs& a);  // writes W_hat [K][N] into a.out (act dtype)
-hipError_t launch_skinny(const GemmArgs& a);   // M <= 64
+hipError_t launch_decode(const GemmArgs& a);   // any M, in launches of up to 64 rows
 hipError_t launch_tiled(const GemmArgs& a);    // M > 64
-const char* skinny_name(int M);
+size_t tiled_workspace_bytes(int M, int K, int N);
+const char* decode_name(int M, int K, int N, int group_size, int act);
 const char* tiled_name(int M, int K, int N);
 bool tiled_supported(const GemmArgs& a);
 

@@ -7,5 +7,6 @@ namespace w4a16 {
 bool tiled_supported(const GemmArgs&) { return false; }
 const char* tiled_name(int, int, int) { return "w4a16_tiled_unavailable"; }
 hipError_t launch_tiled(const GemmArgs&) { return hipErrorNotSupported; }
+size_t tiled_workspace_bytes(int, int, int) { return 0; }
 
 }  // namespace w4a16
