@@ -82,6 +82,16 @@ SMALL = [
     (12, 448, 48, 64, "f16", "nf4"),
     (2, 256, 32, 64, "bf16", "nf4"),
     (70, 256, 32, 64, "f16", "nf4"),
+    # batched kernel (M > 64): ragged M, N not a multiple of the 256-column tile, ragged K,
+    # and K long enough to be split across workgroups (K >= 2048)
+    (65, 256, 48, 128, "f16", "asym"),
+    (128, 384, 272, 32, "f16", "asym"),
+    (200, 2048, 64, 128, "f16", "asym"),
+    (130, 2144, 96, 32, "bf16", "asym"),
+    (97, 2080, 48, 32, "f16", "sym"),
+    (256, 512, 256, 64, "f16", "nf4"),
+    (300, 1024, 128, 128, "bf16", "sym"),
+    (129, 2048, 32, 64, "bf16", "nf4"),
 ]
 
 
@@ -222,7 +232,8 @@ def test_graph_replays_match_eager():
     work and synchronisation between replays, must equal the eager result bit for bit."""
     import weight_only_int4_w4a16_amd as w4
     torch = torch_mod()
-    cases = [rtn_case(1, 1024, 256, 128, seed=11), rtn_case(4, 512, 128, 32, seed=12)]
+    cases = [rtn_case(1, 1024, 256, 128, seed=11), rtn_case(4, 512, 128, 32, seed=12),
+             rtn_case(130, 2048, 64, 128, seed=13)]     # batched kernel, K split in two
     devs = [device_inputs(c) for c in cases]
     outs = [torch.empty((c["M"], c["N"]), dtype=torch.float16, device="cuda") for c in cases]
 

@@ -17,7 +17,7 @@ F16, BF16, F32 = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 
 _lib = None
-_workspaces = {}   # device index -> zero-filled uint8 tensor
+_workspaces = {}   # device index -> uint8 scratch tensor
 
 
 class W4A16Error(RuntimeError):
@@ -101,10 +101,10 @@ def workspace_bytes(M: int, K: int, N: int, group_size: int) -> int:
 
 
 def _workspace(device, nbytes: int, workspace=None):
-    """The caller's workspace, or a cached zero-filled buffer for the device.
+    """The caller's workspace, or a cached scratch buffer for the device.
 
-    The library leaves a workspace zero-filled after every call, so one buffer serves all
-    calls that do not run concurrently; callers that launch GEMMs on several streams at
+    The library keeps nothing in a workspace between calls, so one buffer serves all calls
+    that do not run concurrently; callers that launch GEMMs on several streams at
     once pass their own ``workspace`` per stream. It is never allocated while a HIP graph
     is being captured (warm up eagerly first).
     """
@@ -119,7 +119,7 @@ def _workspace(device, nbytes: int, workspace=None):
         if torch.cuda.is_current_stream_capturing():
             raise W4A16Error("workspace must be allocated before graph capture: run the same "
                              "calls once eagerly on this stream first", ERR_WORKSPACE)
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -142,7 +142,7 @@ def gemm(x, packed, scales, qzeros, group_size: int, out_dtype=None, out=None, w
     """``y = x @ W_hat`` with affine (``qzeros`` given) or symmetric (``qzeros=None``) INT4.
 
     ``x[M, K]`` fp16/bf16, ``scales[K/g, N]`` in x's dtype, ``qzeros[K/g, N/8]`` int32.
-    ``workspace``: optional zero-filled uint8 device tensor (see ``workspace_bytes``).
+    ``workspace``: optional uint8 device tensor of ``workspace_bytes(M, K, N, group_size)``.
     """
     torch = _torch()
     M, K = x.shape

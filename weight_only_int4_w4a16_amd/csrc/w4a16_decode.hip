@@ -22,38 +22,62 @@ int cu_count() {
 constexpr size_t kXldsBytes = 128 * 1024;  // largest x staged in LDS per workgroup
 constexpr size_t kMaxLds = 160 * 1024;     // LDS per compute unit on gfx950
 
-// Launch geometry. SW: with x in LDS and one 16-row tile, the widest tile (4 strips for
-// fp16 with 128-k groups, else 2) that still leaves at least one tile per compute unit;
-// otherwise 1. W: enough waves for about 16 per compute unit, capped so that every wave
-// streams at least one whole group.
-DecodeConfig geometry(int M, int K, int N, int group_size, int act, bool x_in_lds) {
+// Launch geometry for a given tile width SW and wave count W per workgroup.
+DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
   DecodeConfig c;
   c.KC = ceil_div(K, 128);
   c.NT = N / 16;
   c.rows = M < 64 ? M : 64;
   c.MT = ceil_div(c.rows, 16);
   c.x_in_lds = x_in_lds;
-  const int cus = cu_count();
-  const int wmax = c.MT == 1 ? kMaxWavesMt1 : kMaxWavesMtN;
-  c.SW = 1;
-  if (c.x_in_lds && c.MT == 1) {
-    if (act == ACT_F16 && group_size == 128 && c.NT % 4 == 0 && c.NT / 4 >= cus) c.SW = 4;
-    else if (c.NT % 2 == 0 && c.NT / 2 >= cus) c.SW = 2;
-  }
-  c.tiles = c.NT / c.SW;
-  const int D = c.x_in_lds ? 4 / c.SW : 1;  // k-blocks per pipeline group
-  int W = ceil_div(16 * cus, c.tiles);
-  const int wfull = c.KC / D;  // waves that each still get a whole group
-  if (W > wfull) W = wfull;
-  if (W > wmax) W = wmax;
-  if (W < 1) W = 1;
+  c.SW = SW;
+  c.tiles = c.NT / SW;
   c.slice = ceil_div(c.KC, W);
   c.W = ceil_div(c.KC, c.slice);  // drop waves left without blocks
   c.xstride = c.slice * 128 + 8;
-  c.xslice = c.x_in_lds ? c.rows * c.xstride : 0;
-  c.lds_bytes = (size_t)c.W * c.SW * c.rows * 16 * 4 + (size_t)c.W * c.xslice * 2;
+  c.xslice = x_in_lds ? c.rows * c.xstride : 0;
+  c.lds_bytes = (size_t)c.W * SW * c.rows * 16 * 4 + (size_t)c.W * c.xslice * 2;
   c.workspace_bytes = 0;
   return c;
+}
+
+// Pick SW and W. The kernels are built for at least 16 resident waves per compute unit
+// with one 16-row tile (8 with more), so a launch of `tiles` workgroups of W waves runs in
+// ceil(tiles / (CUs * workgroups per CU)) rounds; each round costs about the groups one
+// wave streams plus a fixed latency of about two groups. The cheapest choice wins, wider
+// tiles (shared activation fragments and scale lines) and then more waves on ties.
+// Tiles wider than one strip exist only with x in LDS and one 16-row tile: 4 strips for
+// fp16 with 128-k groups, 2 otherwise (the register-spill-free instantiations).
+DecodeConfig choose(int M, int K, int N, int group_size, int act, bool x_in_lds) {
+  const int KC = ceil_div(K, 128), NT = N / 16;
+  const int rows = M < 64 ? M : 64, MT = ceil_div(rows, 16);
+  const int cus = cu_count();
+  const int waves_per_cu = MT == 1 ? 16 : 8;
+  const int wmax = MT == 1 ? kMaxWavesMt1 : kMaxWavesMtN;
+  DecodeConfig best{};
+  long best_cost = -1;
+  for (int SW = 4; SW >= 1; SW >>= 1) {
+    if (NT % SW) continue;
+    if (SW > 1 && !(x_in_lds && MT == 1)) continue;
+    if (SW == 4 && !(act == ACT_F16 && group_size == 128)) continue;
+    const int D = x_in_lds ? 4 / SW : 1;  // k-blocks per pipeline group
+    for (int W = wmax; W >= 1; W >>= 1) {
+      if (W > 1 && W > KC / D) continue;  // every wave streams at least one whole group
+      const DecodeConfig c = geometry(M, K, N, x_in_lds, SW, W);
+      if (c.lds_bytes > kMaxLds) continue;
+      int wg_per_cu = waves_per_cu / W;
+      const int by_lds = (int)(kMaxLds / c.lds_bytes);
+      if (by_lds < wg_per_cu) wg_per_cu = by_lds;
+      if (wg_per_cu < 1) wg_per_cu = 1;
+      const long rounds = ceil_div(c.tiles, cus * wg_per_cu);
+      const long cost = rounds * (ceil_div(c.slice, D) + 2);
+      if (best_cost < 0 || cost < best_cost) {
+        best = c;
+        best_cost = cost;
+      }
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -63,10 +87,10 @@ DecodeConfig decode_config(int M, int K, int N, int group_size, int act) {
   const int rows = M < 64 ? M : 64;
   const size_t xbytes = (size_t)rows * ceil_div(K, 128) * 128 * 2;
   if (xbytes <= kXldsBytes) {
-    const DecodeConfig c = geometry(M, K, N, group_size, act, true);
-    if (c.lds_bytes <= kMaxLds) return c;
+    const DecodeConfig c = choose(M, K, N, group_size, act, true);
+    if (c.W > 0) return c;
   }
-  return geometry(M, K, N, group_size, act, false);
+  return choose(M, K, N, group_size, act, false);
 }
 
 const char* decode_name(int M, int K, int N, int group_size, int act) {

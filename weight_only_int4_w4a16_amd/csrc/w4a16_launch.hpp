@@ -20,7 +20,7 @@ struct GemmArgs {
   int group_size;
   void* out;
   int out_dtype;           // 0 fp16, 1 bf16, 2 fp32
-  void* workspace;         // zero-filled before first use; left zero-filled after each call
+  void* workspace;         // scratch for split-K partial tiles (no state between calls)
   size_t workspace_bytes;
   hipStream_t stream;
 };
