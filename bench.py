@@ -123,13 +123,17 @@ def build_workload(spec, M, torch, w4, synth):
     return layers, xs, ys, codebook
 
 
-def make_step(spec, layers, xs, ys, codebook, w4):
+def make_step(spec, layers, xs, ys, codebook, w4, only=None):
+    """One pass over every (layer, linear); with ``only`` = a linear index, that linear of
+    every layer."""
     g = spec["g"]
     nf4 = spec.get("nf4", False)
 
     def step():
         for lin in layers:
             for si, L in enumerate(lin):
+                if only is not None and si != only:
+                    continue
                 if nf4:
                     w4.gemm_nf4(xs[si], L["packed"], L["scales"], codebook, g, out=ys[si])
                 else:
@@ -137,9 +141,9 @@ def make_step(spec, layers, xs, ys, codebook, w4):
     return step
 
 
-def cpu_baseline(spec, M, budget_s=20.0):
-    """Time the CPU oracle (dequantize + fp64 matmul, as written) on layer 0's linears,
-    stopping once ``budget_s`` of CPU time has been spent (at least one linear)."""
+def cpu_baseline(spec, M, budget_s=12.0):
+    """Time the CPU oracle (dequantize + fp64 matmul, as written) on the linears of layers
+    0, 1, ... in order, stopping once ``budget_s`` of CPU time has been spent."""
     import numpy as np
 
     import oracle
@@ -152,8 +156,10 @@ def cpu_baseline(spec, M, budget_s=20.0):
     act = spec["act"]
     nf4 = spec.get("nf4", False)
     done_bytes, done_s, names = 0, 0.0, []
-    for si, (K, N) in enumerate(spec["shapes"]):
-        seed = synth.seed_for(spec["config"], si, 0, 0)
+    todo = [(layer, si) for layer in range(spec["layers"]) for si in range(len(spec["shapes"]))]
+    for layer, si in todo:
+        K, N = spec["shapes"][si]
+        seed = synth.seed_for(spec["config"], si, 0, layer)
         qw, sc, qz = synth.timing_weights(K, N, spec["g"], seed, symmetric=spec["sym"],
                                           scale_dtype=act if not nf4 else "f16")
         x = synth.activations(M, K, synth.seed_for(spec["config"], si, synth.ROLE_X), act)
@@ -166,15 +172,15 @@ def cpu_baseline(spec, M, budget_s=20.0):
         dt = time.perf_counter() - t0
         done_s += dt
         done_bytes += algo_bytes(M, K, N, spec["g"], qz is not None, nf4)
-        names.append(spec["names"][si])
+        names.append(f"{layer}.{spec['names'][si]}")
         del w_hat
         if done_s >= budget_s:
             break
     return {"value": round(done_bytes / done_s / 1e9, 4), "unit": "GB/s",
             "cores": int(blas_threads), "kind": "oracle",
-            "sample": (f"layer 0 linears {'+'.join(names)} of {spec['name']} at M={M}, "
-                       f"one pass each ({done_s:.1f} s); NumPy dequant on 1 thread, "
-                       f"fp64 matmul on {blas_threads} BLAS threads")}
+            "sample": (f"{len(names)} linears of {spec['name']} at M={M} (layer.linear "
+                       f"{names[0]} .. {names[-1]}), one pass each, {done_s:.1f} s; NumPy "
+                       f"dequant on 1 thread, fp64 matmul on {blas_threads} BLAS threads")}
 
 
 def main() -> int:
@@ -209,48 +215,64 @@ def main() -> int:
     zeros = not spec["sym"]
     step_bytes = sum(algo_bytes(M, K, N, spec["g"], zeros, nf4) for K, N in launches)
     step_flops = sum(2 * M * N * K for K, N in launches)
-    kernel = w4.kernel_name(M, spec["shapes"][0][0], spec["shapes"][0][1], spec["g"])
 
-    # warm-up eagerly once (also checks every call succeeds), then capture the step
-    step()
-    torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
+    def capture(fn):
+        """Warm up eagerly on a side stream, then capture ``fn`` as a HIP graph."""
+        fn()
+        torch.cuda.synchronize()
+        if args.no_graph:
+            return fn
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            step()
+            fn()
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
+            fn()
         torch.cuda.synchronize()
-    run = graph.replay if graph is not None else step
+        return graph.replay
 
+    def timed(run, reps):
+        """HIP events on the stream the replays run on, around ``reps`` back-to-back runs."""
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            run()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1)
+
+    run = capture(step)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        run()
-    ev1.record()
-    torch.cuda.synchronize()
+    gpu_ms = timed(run, args.steps)
     wall_s = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
 
-    # the step is made of this one kernel only: its average launch duration is the event
-    # time of the timed region over the number of launches (dispatch gaps included)
-    n_launch = len(launches) * args.steps
-    avg_launch_us = gpu_ms * 1e3 / n_launch
-    bytes_per_launch = step_bytes / len(launches)
-    flops_per_launch = step_flops / len(launches)
+    # Per linear: the same launches with only that linear of every layer, timed the same
+    # way. The dominant kernel (most time per step) gets the roofline object.
     mem_bound = M <= 64
+    per_shape = []
+    for si, (K, N) in enumerate(spec["shapes"]):
+        r = capture(make_step(spec, layers, xs, ys, codebook, w4, only=si))
+        r()
+        us = timed(r, args.steps) * 1e3 / (args.steps * spec["layers"])
+        b = algo_bytes(M, K, N, spec["g"], zeros, nf4)
+        per_shape.append({"linear": spec["names"][si], "K": K, "N": N,
+                          "kernel": w4.kernel_name(M, K, N, spec["g"]), "us": round(us, 3),
+                          "GB/s": round(b / us / 1e3, 1),
+                          "TFLOP/s": round(2 * M * N * K / us / 1e6, 2)})
+    dom = max(range(len(per_shape)), key=lambda i: per_shape[i]["us"])
+    K, N = spec["shapes"][dom]
+    kernel = per_shape[dom]["kernel"]
+    avg_launch_us = per_shape[dom]["us"]
+    bytes_per_launch = algo_bytes(M, K, N, spec["g"], zeros, nf4)
+    flops_per_launch = 2 * M * N * K
     if mem_bound:
         achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -261,8 +283,10 @@ def main() -> int:
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
     roof["traffic"] = load_traffic(kernel, args.workload, M)
     roof["kernel"] = kernel
-    roof["avg_launch_us"] = round(avg_launch_us, 3)
+    roof["linear"] = f"{spec['names'][dom]} {K}x{N}"
+    roof["avg_launch_us"] = avg_launch_us
     roof["algo_bytes_per_launch"] = int(bytes_per_launch)
+    roof["algo_flops_per_launch"] = int(flops_per_launch)
 
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     tflops = step_flops / (ms_per_step * 1e-3) / 1e12
@@ -280,12 +304,13 @@ def main() -> int:
         "config": {"workload": args.workload, "M": M, "shapes_KxN": spec["shapes"],
                    "layers": spec["layers"], "group_size": spec["g"],
                    "format": "nf4" if nf4 else ("sym" if spec["sym"] else "asym"),
-                   "launches_per_step": len(launches), "graph": graph is not None,
+                   "launches_per_step": len(launches), "graph": not args.no_graph,
                    "weight_set_GB": round(step_bytes / 1e9, 3)},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tflops": round(tflops, 2),
         "wall_s": round(wall_s, 4),
         "roofline": roof,
+        "per_linear": per_shape,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, M)
