@@ -105,7 +105,11 @@ w4a16_status w4a16_gemm_nf4(const void* x, int M, int K, int N, w4a16_dtype act,
                             void* stream);
 
 /* Test hook: write W_hat[K][N] (row-major, in `wdtype` = F16 or BF16) using the same
- * device dequantization routine the GEMM kernels use. scales are in wdtype. */
+ * device dequantization routine the GEMM kernels use where they form W_hat (the batched
+ * kernel, and the decode kernel for bf16 activations and NF4). The fp16 affine decode
+ * kernel multiplies the exact integers (q - z) and applies s to the fp32 sum of each
+ * group, which skips W_hat's rounding to fp16: its result differs from the rounded-W_hat
+ * product by rounding noise only, within the 1e-3 bound. scales are in wdtype. */
 w4a16_status w4a16_dequant(const int32_t* packed, const void* scales, const int32_t* qzeros,
                            int K, int N, int group_size, w4a16_dtype wdtype, void* w_out,
                            void* stream);

@@ -82,6 +82,10 @@ SMALL = [
     (12, 448, 48, 64, "f16", "nf4"),
     (2, 256, 32, 64, "bf16", "nf4"),
     (70, 256, 32, 64, "f16", "nf4"),
+    # decode launches with activations too large for LDS (at most 32 rows per launch)
+    (50, 8192, 32, 128, "f16", "asym"),
+    (40, 4160, 48, 64, "bf16", "sym"),
+    (20, 8320, 32, 32, "f16", "asym"),
     # batched kernel (M > 64): ragged M, N not a multiple of the 256-column tile, ragged K,
     # and K long enough to be split across workgroups (K >= 2048)
     (65, 256, 48, 128, "f16", "asym"),

@@ -41,25 +41,25 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
   return c;
 }
 
-// Pick SW and W. The kernels are built for at least 16 resident waves per compute unit
-// with one 16-row tile (8 with more), so a launch of `tiles` workgroups of W waves runs in
-// ceil(tiles / (CUs * workgroups per CU)) rounds; each round costs about the groups one
-// wave streams plus a fixed latency of about two groups. The cheapest choice wins, wider
-// tiles (shared activation fragments and scale lines) and then more waves on ties.
-// Tiles wider than one strip exist only with x in LDS and one 16-row tile: 4 strips for
-// fp16 with 128-k groups, 2 otherwise (the register-spill-free instantiations).
-DecodeConfig choose(int M, int K, int N, int group_size, int act, bool x_in_lds) {
+// Pick SW and W. A launch of `tiles` workgroups of W waves runs in
+// ceil(tiles / (CUs * workgroups per CU)) rounds (resident waves per compute unit: 16 for
+// 1024-thread instantiations, which stay within 128 registers, else 8); each round costs
+// about the groups one wave streams plus a fixed latency of about two groups. The cheapest
+// choice wins, wider tiles (shared activation fragments and scale lines) and then more
+// waves on ties. Two-strip tiles exist for x in LDS, one 16-row tile and one scale group per
+// k-block (the register-spill-free instantiations).
+DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
   const int KC = ceil_div(K, 128), NT = N / 16;
   const int rows = M < 64 ? M : 64, MT = ceil_div(rows, 16);
+  const int GPC = 128 / group_size;
   const int cus = cu_count();
-  const int waves_per_cu = MT == 1 ? 16 : 8;
-  const int wmax = MT == 1 ? kMaxWavesMt1 : kMaxWavesMtN;
+  const int wmax = decode_block_threads(MT, GPC, x_in_lds) / 64;
+  const int waves_per_cu = wmax == 16 ? 16 : 8;
   DecodeConfig best{};
   long best_cost = -1;
-  for (int SW = 4; SW >= 1; SW >>= 1) {
+  for (int SW = 2; SW >= 1; SW >>= 1) {
     if (NT % SW) continue;
-    if (SW > 1 && !(x_in_lds && MT == 1)) continue;
-    if (SW == 4 && !(act == ACT_F16 && group_size == 128)) continue;
+    if (SW > 1 && !(x_in_lds && MT == 1 && GPC == 1)) continue;
     const int D = x_in_lds ? 4 / SW : 1;  // k-blocks per pipeline group
     for (int W = wmax; W >= 1; W >>= 1) {
       if (W > 1 && W > KC / D) continue;  // every wave streams at least one whole group
@@ -84,13 +84,24 @@ DecodeConfig choose(int M, int K, int N, int group_size, int act, bool x_in_lds)
 
 // x goes to LDS when it fits beside the reduction area; otherwise it is read per k-block
 DecodeConfig decode_config(int M, int K, int N, int group_size, int act) {
+  (void)act;  // every instantiated configuration exists for both activation types
   const int rows = M < 64 ? M : 64;
   const size_t xbytes = (size_t)rows * ceil_div(K, 128) * 128 * 2;
   if (xbytes <= kXldsBytes) {
-    const DecodeConfig c = choose(M, K, N, group_size, act, true);
+    const DecodeConfig c = choose(M, K, N, group_size, true);
     if (c.W > 0) return c;
   }
-  return choose(M, K, N, group_size, act, false);
+  return choose(M, K, N, group_size, false);
+}
+
+// Rows of x one launch takes: up to 64 when the activations fit in LDS; with activation
+// fragments held in registers at most 32 (two 16-row tiles), which keeps every
+// instantiation within its registers.
+DecodeConfig decode_launch_config(int M, int K, int N, int group_size, int act) {
+  const int rows = M < 64 ? M : 64;
+  DecodeConfig c = decode_config(rows, K, N, group_size, act);
+  if (!c.x_in_lds && rows > 32) c = decode_config(32, K, N, group_size, act);
+  return c;
 }
 
 const char* decode_name(int M, int K, int N, int group_size, int act) {
@@ -98,15 +109,15 @@ const char* decode_name(int M, int K, int N, int group_size, int act) {
       {"w4a16_decode_mt1_sw1", "w4a16_decode_mt1_sw2", "w4a16_decode_mt1_sw4"},
       {"w4a16_decode_mt2_sw1", "w4a16_decode_mt2_sw2", "w4a16_decode_mt2_sw4"},
       {"w4a16_decode_mt4_sw1", "w4a16_decode_mt4_sw2", "w4a16_decode_mt4_sw4"}};
-  const DecodeConfig c = decode_config(M, K, N, group_size, act);
+  const DecodeConfig c = decode_launch_config(M, K, N, group_size, act);
   return names[c.MT == 1 ? 0 : c.MT == 2 ? 1 : 2][c.SW == 1 ? 0 : c.SW == 2 ? 1 : 2];
 }
 
 hipError_t launch_decode(const GemmArgs& a) {
   const size_t osz = a.out_dtype == 2 ? 4 : 2;
-  for (int r0 = 0; r0 < a.M; r0 += 64) {
-    const int rows = a.M - r0 < 64 ? a.M - r0 : 64;
-    const DecodeConfig c = decode_config(rows, a.K, a.N, a.group_size, a.act);
+  for (int r0 = 0; r0 < a.M;) {
+    const DecodeConfig c = decode_launch_config(a.M - r0, a.K, a.N, a.group_size, a.act);
+    const int rows = c.rows;
     DecodeParams p;
     p.x = static_cast<const uint16_t*>(a.x) + (size_t)r0 * a.K;
     p.M = rows;
@@ -138,6 +149,7 @@ hipError_t launch_decode(const GemmArgs& a) {
                           : decode_dispatch<ACT_BF16, FMT_SYM>(p, c, a.stream);
     }
     if (e != hipSuccess) return e;
+    r0 += rows;
   }
   return hipSuccess;
 }

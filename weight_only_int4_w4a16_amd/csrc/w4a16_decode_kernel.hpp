@@ -16,7 +16,8 @@
 // Pipeline. A wave moves its slice in groups of D k-blocks x SW strips (4 blocks, i.e.
 // 4 KiB) with two register sets: group t+1 is in flight while group t is dequantized and
 // multiplied, and every group's loads are issued together, so the in-order load counter
-// never makes one set wait for the other.
+// never makes one set wait for the other. The first two groups are issued before the
+// activations are written to LDS, so that copy costs no extra memory latency.
 //
 // Activations. When x fits, each wave copies the k-slice of x it needs into its own LDS
 // region (no barrier) and reads the MFMA A fragments from there; one fragment serves all
@@ -60,6 +61,20 @@ struct DecodeParams {
   int GPC;       // scale groups per 128-k block (128 / group size)
 };
 
+constexpr int kXRegs = 2;  // 16-byte chunks of x per lane staged in registers ahead of the weights
+
+// Largest workgroup of an instantiation, 1024 or 512 threads. 1024 caps a lane at 128
+// registers (4 waves per SIMD); instantiations that need more (several 16-row tiles, four
+// scale groups per k-block, or activation fragments held in registers) get 512.
+constexpr int decode_block_threads(int MT, int GPC, bool XL) {
+  return MT == 1 && GPC <= 2 && XL ? 1024 : 512;
+}
+
+// fp16 affine formats with at most two 16-row tiles multiply integer-valued operands and
+// apply the group scale to the fp32 partial sums; otherwise W_hat is formed in registers
+// with its one rounding to the activation type.
+constexpr bool decode_defers_scale(int ACT, int FMT, int MT) { return ACT == 0 && FMT != 2 && MT <= 2; }
+
 // workgroup -> tile: tiles [start(x), start(x) + count(x)) run on XCD x = blockIdx % 8
 __device__ __forceinline__ int tile_of(int b, int G) {
   const int q = G >> 3, r = G & 7, x = b & 7;
@@ -72,6 +87,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   constexpr int D = XL ? 4 / SW : 1;  // k-blocks per group
   constexpr int SPG = 4 / GPC;        // 32-k steps per scale group
   constexpr bool ZEROS = FMT == FMT_ASYM;
+  constexpr bool DEFER = decode_defers_scale(ACT, FMT, MT);
 
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
@@ -126,6 +142,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   };
 
   f4_t acc[SW][MT];
+  f4_t part[SW][DEFER ? MT : 1];  // DEFER: the current scale group's sum of x (q - z)
 #pragma unroll
   for (int sw = 0; sw < SW; ++sw)
 #pragma unroll
@@ -161,25 +178,60 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
               a[mt] = __builtin_bit_cast(AT, v);
             }
             const int gi = j / SPG;
+            if constexpr (!DEFER) {
 #pragma unroll
-            for (int sw = 0; sw < SW; ++sw) {
-              const uint32_t w = b[d][sw][j];
-              const uint32_t sraw = s[d][sw][gi];
-              AT bf;
-              if constexpr (FMT == FMT_NF4) {
-                if constexpr (ACT == ACT_F16)
-                  bf = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
-                else
-                  bf = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
-              } else {
-                const uint32_t zq = ZEROS ? (z[d][sw][gi] >> shift) & 0xFu : 8u;
-                if constexpr (ACT == ACT_F16)
-                  bf = dequant_word_f16(w, make_zero_f16(zq), as_h2(sraw * 0x00010001u));
-                else
-                  bf = dequant_word_bf16(w, make_zero_f32(zq, __builtin_bit_cast(float, sraw << 16)));
+              for (int sw = 0; sw < SW; ++sw) {
+                const uint32_t w = b[d][sw][j];
+                const uint32_t sraw = s[d][sw][gi];
+                AT bf;
+                if constexpr (FMT == FMT_NF4) {
+                  if constexpr (ACT == ACT_F16)
+                    bf = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
+                  else
+                    bf = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
+                } else {
+                  const uint32_t zq = ZEROS ? (z[d][sw][gi] >> shift) & 0xFu : 8u;
+                  if constexpr (ACT == ACT_F16)
+                    bf = dequant_word_f16(w, make_zero_f16(zq), as_h2(sraw * 0x00010001u));
+                  else
+                    bf = dequant_word_bf16(w, make_zero_f32(zq, __builtin_bit_cast(float, sraw << 16)));
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[sw][mt] = mfma16(a[mt], bf, acc[sw][mt]);
               }
+            } else {
+              // affine: integer-valued operands into the group's partial sum, scaled once
+              // when the group's last 32-k step is done
+              const bool first = j % SPG == 0, last = j % SPG == SPG - 1;
 #pragma unroll
-              for (int mt = 0; mt < MT; ++mt) acc[sw][mt] = mfma16(a[mt], bf, acc[sw][mt]);
+              for (int sw = 0; sw < SW; ++sw) {
+                const uint32_t w = b[d][sw][j];
+                const uint32_t zq = ZEROS ? (z[d][sw][gi] >> shift) & 0xFu : 8u;
+                AT bq, bz;
+                if constexpr (ACT == ACT_F16) {
+                  bq = unpack_biased_f16(w);
+                  bz = neg_bias_f16(zq);
+                } else {
+                  bq = unpack_biased_bf16(w);
+                  bz = neg_bias_bf16(zq);
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                  part[sw][mt] = mfma16(a[mt], bq, first ? f4_t{0.f, 0.f, 0.f, 0.f} : part[sw][mt]);
+                  part[sw][mt] = mfma16(a[mt], bz, part[sw][mt]);
+                }
+                if (last) {
+                  const uint32_t sraw = s[d][sw][gi];
+                  const float sf = ACT == ACT_F16
+                                       ? (float)__builtin_bit_cast(_Float16, (uint16_t)sraw)
+                                       : __builtin_bit_cast(float, sraw << 16);
+#pragma unroll
+                  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                      acc[sw][mt][r] = __builtin_fmaf(sf, part[sw][mt][r], acc[sw][mt][r]);
+                }
+              }
             }
           }
         }
@@ -195,26 +247,70 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
     else compute_group(b, s, z, xf, t, std::true_type{});
   };
 
-  if (ng > 0) {
-    load_group(bA, sA, zA, xA, 0);
+  // Activations: this wave's slice of x, up to kXRegs 16-byte chunks per lane staged in
+  // registers; loaded before the first weight groups and written to LDS after them, so the
+  // write waits for the x loads only (the load counter retires in order) while the weight
+  // groups are still in flight.
+  const int kbeg = kc0 * 128;
+  const int cpr = (min(kc1 * 128, K) - kbeg) >> 3;  // 16-byte chunks per row of the slice
+  const int nchunks = XL ? rows * cpr : 0;
+  u4_t xr[kXRegs];
+  int xoff[kXRegs];
+  auto x_load = [&]() {
     if constexpr (XL) {
-      // this wave's k-slice of x -> its LDS region (the first group's loads are already in
-      // flight, so their latency and the copy's overlap)
-      const int kbeg = kc0 * 128;
-      const int chunks = (min(kc1 * 128, K) - kbeg) >> 3;  // 16-byte chunks per row
-      for (int m = 0; m < rows; ++m)
-        for (int c = lane; c < chunks; c += 64)
-          *reinterpret_cast<u4_t*>(xs + (size_t)m * p.xstride + c * 8) =
-              *reinterpret_cast<const u4_t*>(p.x + (size_t)m * K + kbeg + c * 8);
+#pragma unroll
+      for (int i = 0; i < kXRegs; ++i) {
+        // past the end: a copy of the last chunk, stored again to the same place (harmless,
+        // and keeps the store unconditional so the load is not sunk behind the weights)
+        const int c = min(lane + 64 * i, nchunks - 1);
+        const int m = c / cpr, cc = c - (c / cpr) * cpr;
+        xoff[i] = m * p.xstride + cc * 8;
+        xr[i] = *reinterpret_cast<const u4_t*>(p.x + (size_t)m * K + kbeg + cc * 8);
+      }
     }
+  };
+  auto x_store = [&]() {
+    if constexpr (XL) {
+#pragma unroll
+      for (int i = 0; i < kXRegs; ++i) *reinterpret_cast<u4_t*>(xs + xoff[i]) = xr[i];
+      // chunks beyond the register-staged ones (slices of several rows)
+      for (int c = lane + 64 * kXRegs; c < nchunks; c += 64) {
+        const int m = c / cpr, cc = c - (c / cpr) * cpr;
+        *reinterpret_cast<u4_t*>(xs + (size_t)m * p.xstride + cc * 8) =
+            *reinterpret_cast<const u4_t*>(p.x + (size_t)m * K + kbeg + cc * 8);
+      }
+    }
+  };
+
+  // Every path below issues its loads unconditionally, so the compiler's wait before each
+  // group covers exactly the loads issued before that group's (a load issued on only some
+  // paths into a join would make it wait for everything).
+  if (ng == 1) {
+    x_load();
+    load_group(bA, sA, zA, xA, 0);
+    x_store();
+    compute(bA, sA, zA, xA, 0);
+  } else if (ng > 1) {
+    x_load();
+    load_group(bA, sA, zA, xA, 0);
+    load_group(bB, sB, zB, xB, 1);
+    x_store();
     int t = 0;
-    for (; t + 1 < ng; t += 2) {
-      load_group(bB, sB, zB, xB, t + 1);
+    for (; t + 3 < ng; t += 2) {  // groups t+2 and t+3 exist
       compute(bA, sA, zA, xA, t);
-      if (t + 2 < ng) load_group(bA, sA, zA, xA, t + 2);
+      load_group(bA, sA, zA, xA, t + 2);
+      compute(bB, sB, zB, xB, t + 1);
+      load_group(bB, sB, zB, xB, t + 3);
+    }
+    if (t + 2 < ng) {  // three groups left
+      compute(bA, sA, zA, xA, t);
+      load_group(bA, sA, zA, xA, t + 2);
+      compute(bB, sB, zB, xB, t + 1);
+      compute(bA, sA, zA, xA, t + 2);
+    } else {  // two groups left
+      compute(bA, sA, zA, xA, t);
       compute(bB, sB, zB, xB, t + 1);
     }
-    if (t < ng) compute(bA, sA, zA, xA, t);
   }
 
   // ---- sum the W partial tiles in wave order ----
@@ -244,33 +340,23 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
 template <int ACT, int FMT>
 hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s);
 
-constexpr int kMaxWavesMt1 = 16;  // waves per workgroup (1024 threads) for one 16-row tile
-constexpr int kMaxWavesMtN = 8;   // more 16-row tiles: more accumulators per lane
 
 template <int ACT, int MT, int SW, int GPC, int FMT, bool XL>
 hipError_t decode_launch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
-  constexpr int LB = MT == 1 ? 64 * kMaxWavesMt1 : 64 * kMaxWavesMtN;
+  constexpr int LB = decode_block_threads(MT, GPC, XL);
   hipLaunchKernelGGL((decode_kernel<ACT, MT, SW, GPC, FMT, XL, LB>), dim3(c.tiles), dim3(64 * c.W),
                      c.lds_bytes, s, p);
   return hipGetLastError();
 }
 
-// The instantiated set (all free of register spills on gfx950): x in LDS with one 16-row
-// tile: SW 1 or 2, and SW 4 for fp16 with one scale group per k-block; every other case SW 1.
+// The instantiated set (all free of register spills on gfx950): tiles of two strips with x
+// in LDS, one 16-row tile and one scale group per k-block; every other case one strip.
 template <int ACT, int FMT, int MT, bool XL>
 hipError_t decode_dispatch_gpc(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
   if constexpr (MT == 1 && XL) {
-    if (c.SW == 4) {
-      if constexpr (ACT == ACT_F16)
-        if (p.GPC == 1) return decode_launch<ACT, 1, 4, 1, FMT, true>(p, c, s);
-      return hipErrorNotSupported;
-    }
     if (c.SW == 2) {
-      switch (p.GPC) {
-        case 1: return decode_launch<ACT, 1, 2, 1, FMT, true>(p, c, s);
-        case 2: return decode_launch<ACT, 1, 2, 2, FMT, true>(p, c, s);
-        default: return decode_launch<ACT, 1, 2, 4, FMT, true>(p, c, s);
-      }
+      if (p.GPC == 1) return decode_launch<ACT, 1, 2, 1, FMT, true>(p, c, s);
+      return hipErrorNotSupported;
     }
   }
   if (c.SW != 1) return hipErrorNotSupported;
@@ -287,8 +373,8 @@ hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStre
                                    : decode_dispatch_gpc<ACT, FMT, 1, false>(p, c, s);
   if (c.MT == 2) return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 2, true>(p, c, s)
                                    : decode_dispatch_gpc<ACT, FMT, 2, false>(p, c, s);
-  return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 4, true>(p, c, s)
-                    : decode_dispatch_gpc<ACT, FMT, 4, false>(p, c, s);
+  // four 16-row tiles only with x in LDS (launches take at most 32 rows otherwise)
+  return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 4, true>(p, c, s) : hipErrorNotSupported;
 }
 
 }  // namespace w4a16

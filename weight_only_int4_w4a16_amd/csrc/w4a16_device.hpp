@@ -1,7 +1,9 @@
 // w4a16_device.hpp - device-side building blocks shared by every W4A16 kernel on gfx950:
 // the private packed weight layout, nibble unpacking, the one-rounding dequantization and
-// thin MFMA wrappers. Every kernel that produces W_hat calls the routines below, so the
-// dequant test hook and the GEMMs compute bit-identical weights.
+// thin MFMA wrappers. Every kernel that forms W_hat calls the routines below, so the
+// dequant test hook and the GEMMs compute bit-identical weights. (The fp16 affine decode
+// kernel instead multiplies the exact integers q - z and scales the fp32 group sums; see
+// unpack_biased_f16.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -96,6 +98,48 @@ __device__ inline h8_t dequant_word_f16(uint32_t w, ZeroF16 zc, h2_t s2) {
   r[0] = d0[0]; r[1] = d0[1]; r[2] = d1[0]; r[3] = d1[1];
   r[4] = d2[0]; r[5] = d2[1]; r[6] = d3[0]; r[7] = d3[1];
   return r;
+}
+
+// ---------------------------------------------------------------------------------------
+// Integer-valued MFMA operands for the decode kernels (scale applied after the products).
+//
+// unpack_biased_*: the eight codes of a word as exact 16-bit floats biased by a constant
+// (fp16: 1024 + q for the low nibble of each byte, 64 + q for the high one; bf16: 128 + q).
+// neg_bias_*: the matching -(bias + z) for every k of the word. Multiplying x by both and
+// summing in fp32 gives sum_k x_k (q_k - z) over a scale group; the group's scale is then
+// applied to that fp32 partial sum once. All products are exact (an 11- or 8-bit
+// significand times an integer below 2^11), so the only roundings are the fp32 sums.
+// ---------------------------------------------------------------------------------------
+__device__ inline h8_t unpack_biased_f16(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  u4_t r;
+  r[0] = and_or(w, 0x000F000Fu, 0x64006400u);   // (q0, q1) + 1024
+  r[1] = and_or(w, 0x00F000F0u, 0x54005400u);   // (q2, q3) + 64
+  r[2] = and_or(w8, 0x000F000Fu, 0x64006400u);  // (q4, q5) + 1024
+  r[3] = and_or(w8, 0x00F000F0u, 0x54005400u);  // (q6, q7) + 64
+  return __builtin_bit_cast(h8_t, r);
+}
+
+__device__ inline h8_t neg_bias_f16(uint32_t z) {
+  const uint32_t n1024 = (0xE400u | z) * 0x00010001u;         // -(1024 + z), twice
+  const uint32_t n64 = (0xD400u | (z << 4)) * 0x00010001u;    // -(64 + z), twice
+  return __builtin_bit_cast(h8_t, u4_t{n1024, n64, n1024, n64});
+}
+
+__device__ inline b8_t unpack_biased_bf16(uint32_t w) {
+  // device nibble p holds code perm[p] = {0, 2, 4, 6, 1, 3, 5, 7}: bits 0-3 and 16-19 are
+  // codes 0 and 1, bits 4-7 and 20-23 codes 2 and 3, and so on
+  u4_t r;
+  r[0] = and_or(w, 0x000F000Fu, 0x43004300u);          // (q0, q1) + 128
+  r[1] = and_or(w >> 4, 0x000F000Fu, 0x43004300u);     // (q2, q3) + 128
+  r[2] = and_or(w >> 8, 0x000F000Fu, 0x43004300u);     // (q4, q5) + 128
+  r[3] = and_or(w >> 12, 0x000F000Fu, 0x43004300u);    // (q6, q7) + 128
+  return __builtin_bit_cast(b8_t, r);
+}
+
+__device__ inline b8_t neg_bias_bf16(uint32_t z) {
+  const uint32_t n = (0xC300u | z) * 0x00010001u;  // -(128 + z), twice
+  return __builtin_bit_cast(b8_t, u4_t{n, n, n, n});
 }
 
 // ---------------------------------------------------------------------------------------

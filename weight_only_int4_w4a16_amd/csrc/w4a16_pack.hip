@@ -38,7 +38,7 @@ hipError_t launch_pack(const uint32_t* qweight, int K, int N, uint32_t* packed, 
 }
 
 // Dequantization test hook: one thread per (strip, k-block, lane), each word expanded with
-// the same device routine the GEMM kernels use, written to W_hat[K][N].
+// the same device routine the GEMM kernels that form W_hat use, written to W_hat[K][N].
 template <int ACT, bool NF4>
 __global__ __launch_bounds__(256) void dequant_kernel(const u4_t* __restrict__ packed,
                                                       const uint16_t* __restrict__ scales,
