@@ -192,6 +192,9 @@ def main() -> int:
     ap.add_argument("--m", type=int, default=None, help="rows of x (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (x4), the known-size reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -200,6 +203,16 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 4}))
+        return 0
 
     import weight_only_int4_w4a16_amd as w4
     from weight_only_int4_w4a16_amd import synth
