@@ -280,6 +280,15 @@ __device__ inline f4_t mfma16(b8_t a, b8_t b, f4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(32x32, fp32) += A(32x16) * B(16x32). Lane l: A row l%32, k = 8*(l/32)+i; B column l%32,
+// same k; D column l%32, rows 8*(i/4) + 4*(l/32) + i%4, i = 0..15.
+__device__ inline f16v_t mfma32(h8_t a, h8_t b, f16v_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline f16v_t mfma32(b8_t a, b8_t b, f16v_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // fp32 -> output element
 __device__ inline void store_out(void* out, size_t idx, float v, int out_dtype) {
   if (out_dtype == 2) {

@@ -7,12 +7,16 @@
 // tile loop and the 16-bit weight tile never goes to HBM.
 //
 // Tiling. A workgroup of four waves computes a 128 x 256 output tile. Each wave owns 64
-// columns (4 strips of 16) over all 128 rows: per 32-k step it dequantizes one packed
-// word per strip in registers (the packed layout hands each lane exactly its MFMA B
-// operand) and reuses it for 8 row tiles, so the dequantization is spread over 128 rows.
+// columns (two 32-column pairs of strips) over all 128 rows and multiplies with
+// v_mfma_f32_32x32x16_{f16,bf16}, which on gfx950 delivers twice the flops per cycle of the
+// 16x16x32 form. Its B operand gives lane l column l%32 of a pair and k = 8(l/32) + i of a
+// 16-k step. In the packed layout those eight codes are word t/2 of the 16-byte chunk that
+// lane 16*((2t + l/32) % 4) + l%16 of the strip's block owns; lane l loads those two
+// chunks (32 bytes) itself, so every code is loaded once and no lanes exchange data. Each
+// word is dequantized once, in registers, and reused for 4 row tiles (128 rows).
 // The activation tile (128 rows x 128 k, fp16/bf16) is staged in LDS, double-buffered,
 // and shared by the four waves; the A fragment of a row tile is read once per step and
-// used for four strips. Products: v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulators.
+// used for both pairs. Accumulation is fp32.
 //
 // Split-K. When the output tiles alone cannot fill the chip, the K range is cut into S
 // contiguous slices, one workgroup each. Every slice stores its fp32 partial tile in the
@@ -26,10 +30,11 @@ namespace w4a16 {
 namespace {
 
 constexpr int kBM = 128;            // rows per workgroup tile
-constexpr int kStrips = 4;          // 16-column strips per wave
+constexpr int kPairs = 2;           // 32-column strip pairs per wave (4 strips of 16)
+constexpr int kStrips = 2 * kPairs;
 constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kBN = 16 * kStrips * kWaves;  // 256 columns per workgroup tile
-constexpr int kMT = kBM / 16;       // MFMA row tiles per wave
+constexpr int kMT = kBM / 32;       // 32-row MFMA tiles per wave
 constexpr int kAStride = 128 + 8;   // LDS row stride of the activation tile (halves)
 constexpr int kAChunks = kBM * 16 / (64 * kWaves);  // 16-byte chunks per thread per k-block
 constexpr size_t kLdsBytes = 2 * kBM * kAStride * 2;  // double-buffered activation tile
@@ -89,9 +94,9 @@ __global__ __launch_bounds__(256) void tiled_kernel(TiledParams p) {
   struct Regs {
     int kc;
     u4_t a[kAChunks];
-    u4_t b[kStrips];
-    uint32_t s[kStrips][GPC];  // 16-bit scale zero-extended by the load itself
-    uint32_t z[kStrips][GPC];
+    u4_t b[kPairs][2];         // chunks 16h + c and 32 + 16h + c (h = lane/32, c = lane%16)
+    uint32_t s[kPairs][GPC];   // 16-bit scale zero-extended by the load itself
+    uint32_t z[kPairs][GPC];
   };
   auto load = [&](Regs& R, int kc) {
 #pragma unroll
@@ -105,15 +110,19 @@ __global__ __launch_bounds__(256) void tiled_kernel(TiledParams p) {
     }
     R.kc = kc;
 #pragma unroll
-    for (int st = 0; st < kStrips; ++st) {
-      const int nt = min(nt0 + st, p.NT - 1);  // strips past N: loaded in bounds, never stored
+    for (int pr = 0; pr < kPairs; ++pr) {
+      // strips past N: loaded in bounds, never stored
+      const int nt = min(nt0 + 2 * pr + ((lane >> 4) & 1), p.NT - 1);
       const int col = nt * 16 + (lane & 15);
-      R.b[st] = __builtin_nontemporal_load(p.packed + ((size_t)nt * KC + kc) * 64 + lane);
+      const u4_t* blk = p.packed + ((size_t)nt * KC + kc) * 64;
+      const int c0 = 16 * (lane >> 5) + (lane & 15);
+      R.b[pr][0] = __builtin_nontemporal_load(blk + c0);
+      R.b[pr][1] = __builtin_nontemporal_load(blk + c0 + 32);
 #pragma unroll
       for (int gi = 0; gi < GPC; ++gi) {
         const int g = min(kc * GPC + gi, p.NG - 1);
-        R.s[st][gi] = p.scales[(size_t)g * N + col];
-        if constexpr (ZEROS) R.z[st][gi] = p.qzeros[(size_t)g * (N >> 3) + (col >> 3)];
+        R.s[pr][gi] = p.scales[(size_t)g * N + col];
+        if constexpr (ZEROS) R.z[pr][gi] = p.qzeros[(size_t)g * (N >> 3) + (col >> 3)];
       }
     }
   };
@@ -131,42 +140,45 @@ __global__ __launch_bounds__(256) void tiled_kernel(TiledParams p) {
   Nf4Lut lut;
   if constexpr (FMT == FMT_NF4) lut = load_nf4_lut(p.codebook);
 
-  f4_t acc[kMT][kStrips];
+  f16v_t acc[kMT][kPairs];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-    for (int st = 0; st < kStrips; ++st) acc[mt][st] = f4_t{0.f, 0.f, 0.f, 0.f};
+    for (int pr = 0; pr < kPairs; ++pr)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mt][pr][i] = 0.f;
 
   auto compute = [&](const Regs& R, int buf) {
     const uint16_t* as = lds_a + buf * kBM * kAStride;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gi = j / SPG;
-      AT bf[kStrips];
+    for (int t = 0; t < 8; ++t) {  // 16-k steps of the block
+      const int gi = t / (8 / GPC);
+      AT bf[kPairs];
 #pragma unroll
-      for (int st = 0; st < kStrips; ++st) {
-        const uint32_t w = R.b[st][j];
-        const uint32_t sraw = R.s[st][gi];
+      for (int pr = 0; pr < kPairs; ++pr) {
+        const uint32_t w = R.b[pr][t & 1][t >> 1];
+        const uint32_t sraw = R.s[pr][gi];
         if constexpr (FMT == FMT_NF4) {
           if constexpr (ACT == ACT_F16)
-            bf[st] = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
+            bf[pr] = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
           else
-            bf[st] = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
+            bf[pr] = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
         } else {
-          const uint32_t zq = ZEROS ? (R.z[st][gi] >> shift) & 0xFu : 8u;
+          const uint32_t zq = ZEROS ? (R.z[pr][gi] >> shift) & 0xFu : 8u;
           if constexpr (ACT == ACT_F16)
-            bf[st] = dequant_word_f16(w, make_zero_f16(zq), as_h2(sraw * 0x00010001u));
+            bf[pr] = dequant_word_f16(w, make_zero_f16(zq), as_h2(sraw * 0x00010001u));
           else
-            bf[st] = dequant_word_bf16(w, make_zero_f32(zq, __builtin_bit_cast(float, sraw << 16)));
+            bf[pr] = dequant_word_bf16(w, make_zero_f32(zq, __builtin_bit_cast(float, sraw << 16)));
         }
       }
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
+        // A: row 32 mt + l%32, k = 16 t + 8 (l/32) .. +8
         const u4_t a = *reinterpret_cast<const u4_t*>(
-            as + (mt * 16 + (lane & 15)) * kAStride + j * 32 + (lane >> 4) * 8);
+            as + (mt * 32 + (lane & 31)) * kAStride + t * 16 + (lane >> 5) * 8);
 #pragma unroll
-        for (int st = 0; st < kStrips; ++st)
-          acc[mt][st] = mfma16(__builtin_bit_cast(AT, a), bf[st], acc[mt][st]);
+        for (int pr = 0; pr < kPairs; ++pr)
+          acc[mt][pr] = mfma32(__builtin_bit_cast(AT, a), bf[pr], acc[mt][pr]);
       }
     }
   };
@@ -196,37 +208,24 @@ __global__ __launch_bounds__(256) void tiled_kernel(TiledParams p) {
   if (i < nb) compute(R0, 0);
 
   // ---- epilogue ----
-  // lane l holds column 16*strip + l%16 and rows 16*mt + 4*(l/16) + r of each 16x16 tile
-  if (p.S == 1) {
-#pragma unroll
-    for (int st = 0; st < kStrips; ++st) {
-      const int nt = nt0 + st;
-      if (nt < p.NT) {
-        const int col = nt * 16 + (lane & 15);
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = m0 + mt * 16 + 4 * (lane >> 4) + r;
-            if (m < M) store_out(p.out, (size_t)m * N + col, acc[mt][st][r], p.out_dtype);
-          }
-      }
-    }
-    return;
-  }
-  // K split: store this slice's fp32 partial tile; the reduce kernel sums the slices
+  // lane l holds column 32*pair + l%32 and rows 32*mt + 8*(i/4) + 4*(l/32) + i%4, i < 16
   const size_t slice_stride = (size_t)p.tiles_m * kBM * N;
 #pragma unroll
-  for (int st = 0; st < kStrips; ++st) {
-    const int nt = nt0 + st;
+  for (int pr = 0; pr < kPairs; ++pr) {
+    const int nt = nt0 + 2 * pr + ((lane >> 4) & 1);
     if (nt < p.NT) {
       const int col = nt * 16 + (lane & 15);
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + mt * 16 + 4 * (lane >> 4) + r;
-          p.partials[z * slice_stride + (size_t)m * N + col] = acc[mt][st][r];
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + mt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (p.S == 1) {
+            if (m < M) store_out(p.out, (size_t)m * N + col, acc[mt][pr][i], p.out_dtype);
+          } else {
+            // K split: this slice's fp32 partial tile; the reduce kernel sums the slices
+            p.partials[z * slice_stride + (size_t)m * N + col] = acc[mt][pr][i];
+          }
         }
     }
   }
