@@ -6,7 +6,7 @@
 // rows; "INT4 and Low-Bit Inference", section 5 (Marlin): the unpack is fused into the
 // tile loop and the 16-bit weight tile never goes to HBM.
 //
-// Tiling. A workgroup of four waves computes a 128 x 256 output tile. Each wave owns 64
+// Tiling. A workgroup of eight waves (two per SIMD) computes a 128 x 512 output tile. Each wave owns 64
 // columns (two 32-column pairs of strips) over all 128 rows and multiplies with
 // v_mfma_f32_32x32x16_{f16,bf16}, which on gfx950 delivers twice the flops per cycle of the
 // 16x16x32 form. Its B operand gives lane l column l%32 of a pair and k = 8(l/32) + i of a
@@ -32,11 +32,12 @@ namespace {
 constexpr int kBM = 128;            // rows per workgroup tile
 constexpr int kPairs = 2;           // 32-column strip pairs per wave (4 strips of 16)
 constexpr int kStrips = 2 * kPairs;
-constexpr int kWaves = 4;           // waves per workgroup
-constexpr int kBN = 16 * kStrips * kWaves;  // 256 columns per workgroup tile
+constexpr int kWaves = 8;           // waves per workgroup (two per SIMD)
+constexpr int kBN = 16 * kStrips * kWaves;  // 512 columns per workgroup tile
 constexpr int kMT = kBM / 32;       // 32-row MFMA tiles per wave
 constexpr int kAStride = 128 + 8;   // LDS row stride of the activation tile (halves)
-constexpr int kAChunks = kBM * 16 / (64 * kWaves);  // 16-byte chunks per thread per k-block
+constexpr int kThreads = 64 * kWaves;
+constexpr int kAChunks = kBM * 16 / kThreads;  // 16-byte chunks per thread per k-block
 constexpr size_t kLdsBytes = 2 * kBM * kAStride * 2;  // double-buffered activation tile
 
 enum Fmt { FMT_ASYM = 0, FMT_SYM = 1, FMT_NF4 = 2 };
@@ -70,7 +71,7 @@ __device__ __forceinline__ int tile_of(int b, int G) {
 }
 
 template <int ACT, int GPC, int FMT>
-__global__ __launch_bounds__(256) void tiled_kernel(TiledParams p) {
+__global__ __launch_bounds__(kThreads) void tiled_kernel(TiledParams p) {
   typedef typename ActT<ACT>::type AT;
   constexpr int SPG = 4 / GPC;
   constexpr bool ZEROS = FMT == FMT_ASYM;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(TiledParams p) {
   auto load = [&](Regs& R, int kc) {
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + kThreads * i;
       const int row = c >> 4, kch = c & 15;
       const int gm = min(m0 + row, M - 1);
       const int k = kc * 128 + kch * 8;
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(TiledParams p) {
   auto store_a = [&](const Regs& R, int buf) {
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + kThreads * i;
       const int row = c >> 4, kch = c & 15;
       const bool in_k = R.kc * 128 + kch * 8 < K;
       *reinterpret_cast<u4_t*>(lds_a + buf * kBM * kAStride + row * kAStride + kch * 8) =
@@ -283,11 +284,11 @@ TiledGeometry tiled_geometry(int M, int K, int N) {
 template <int ACT, int GPC>
 hipError_t launch_fmt(const GemmArgs& a, const TiledParams& p, dim3 grid) {
   if (a.nf4)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4>), grid, dim3(256), kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4>), grid, dim3(kThreads), kLdsBytes, a.stream, p);
   else if (a.qzeros)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM>), grid, dim3(256), kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM>), grid, dim3(kThreads), kLdsBytes, a.stream, p);
   else
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM>), grid, dim3(256), kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM>), grid, dim3(kThreads), kLdsBytes, a.stream, p);
   return hipGetLastError();
 }
 
@@ -305,7 +306,7 @@ hipError_t launch_gpc(const GemmArgs& a, const TiledParams& p, dim3 grid) {
 bool tiled_supported(const GemmArgs&) { return true; }
 
 const char* tiled_name(int M, int K, int N) {
-  return tiled_geometry(M, K, N).S > 1 ? "w4a16_tiled_128x256_splitk" : "w4a16_tiled_128x256";
+  return tiled_geometry(M, K, N).S > 1 ? "w4a16_tiled_128x512_splitk" : "w4a16_tiled_128x512";
 }
 
 size_t tiled_workspace_bytes(int M, int K, int N) {
