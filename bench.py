@@ -183,6 +183,118 @@ def cpu_baseline(spec, M, budget_s=12.0):
                        f"dequant on 1 thread, fp64 matmul on {blas_threads} BLAS threads")}
 
 
+SWEEP = [
+    # (config name, format, group, act, [(K, N)], [M])
+    ("c1 gemv", "asym", 128, "f16", [(4096, 4096)], [1]),
+    ("c2 llama3-8b", "asym", 128, "f16", [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096)],
+     [1, 4, 16]),
+    ("c3 llama3-70b", "sym", 128, "f16", [(8192, 10240), (8192, 8192), (8192, 57344), (28672, 8192)],
+     [1, 8, 32]),
+    ("c4 crossover g128", "asym", 128, "f16", [(4096, 14336)], [1, 2, 4, 8, 16, 32, 64, 128, 256]),
+    ("c4 crossover g32", "asym", 32, "f16", [(4096, 14336)], [1, 2, 4, 8, 16, 32, 64, 128, 256]),
+    ("c4 crossover nf4", "nf4", 64, "f16", [(4096, 14336)], [1, 2, 4, 8, 16, 32, 64, 128, 256]),
+    ("c5 prefill bf16", "asym", 128, "bf16", [(8192, 28672)], [2048]),
+]
+
+
+def sweep(args, torch, w4) -> int:
+    """Per (config, shape, M): one GEMM per weight copy, enough copies (>= 600 MB) that the
+    weights stream from HBM, replayed from a HIP graph and timed with HIP events. Weights are
+    seeded random codes / scales drawn on the device (timing does not depend on values).
+    Prints one JSON line per row; at the prefill shape also a dense 16-bit torch.matmul
+    (hipBLASLt) and the naive path (dequantize to HBM with the test hook, then matmul)."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261203)
+    codebook = None
+    for name, fmt, g, act, shapes, Ms in SWEEP:
+        tdt = torch.float16 if act == "f16" else torch.bfloat16
+        nf4 = fmt == "nf4"
+        for K, N in shapes:
+            wbytes = algo_bytes(0, K, N, g, fmt == "asym", nf4)
+            copies = max(2, -(-600_000_000 // wbytes))
+            bufs = []
+            for _ in range(copies):
+                qw = torch.randint(-2**31, 2**31 - 1, (K // 8, N), dtype=torch.int32, device=dev,
+                                   generator=gen)
+                packed = w4.pack(qw)
+                del qw
+                sdt = torch.float16 if nf4 else tdt
+                sc = (torch.rand((K // g, N), device=dev, generator=gen) * 0.005 + 0.004).to(sdt)
+                qz = (torch.randint(-2**31, 2**31 - 1, (K // g, N // 8), dtype=torch.int32,
+                                    device=dev, generator=gen) if fmt == "asym" else None)
+                bufs.append((packed, sc, qz))
+            if nf4 and codebook is None:
+                import numpy as np
+                vals = np.loadtxt(os.path.join(ROOT, "tests", "golden", "nf4_codebook.txt"))
+                codebook = torch.from_numpy(vals.astype(np.float16)).to(dev)
+            for M in Ms:
+                x = torch.randn((M, K), device=dev, generator=gen).to(tdt)
+                y = torch.empty((M, N), device=dev, dtype=tdt)
+
+                def step():
+                    for packed, sc, qz in bufs:
+                        if nf4:
+                            w4.gemm_nf4(x, packed, sc, codebook, g, out=y)
+                        else:
+                            w4.gemm(x, packed, sc, qz, g, out=y)
+                step()
+                torch.cuda.synchronize()
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    step()
+                torch.cuda.current_stream().wait_stream(s)
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    step()
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                reps = max(2, min(args.steps, int(2e5 / (copies * max(1.0, M * K * N / 1e9)))))
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+                b = algo_bytes(M, K, N, g, fmt == "asym", nf4)
+                fl = 2.0 * M * N * K
+                t_roof = max(b / (HBM_PEAK_GBS * 1e3), fl / (MFMA_F16_PEAK_TFLOPS * 1e6))
+                row = {"config": name, "format": fmt, "group": g, "act": act, "M": M, "K": K, "N": N,
+                       "kernel": w4.kernel_name(M, K, N, g), "us": round(us, 2),
+                       "GB/s": round(b / us / 1e3, 1), "TFLOP/s": round(fl / us / 1e6, 1),
+                       "roof_frac": round(t_roof / us, 3)}
+                if name.startswith("c5"):
+                    wd = torch.randn((K, N), device=dev, generator=gen).to(tdt)
+                    for _ in range(3):
+                        torch.matmul(x, wd)
+                    torch.cuda.synchronize()
+                    e0.record()
+                    for _ in range(reps):
+                        torch.matmul(x, wd)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    row["dense_matmul_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+                    del wd
+                    packed, sc, qz = bufs[0]
+                    w4.dequant(packed, sc, qz, K, g)  # warm
+                    torch.cuda.synchronize()
+                    e0.record()
+                    for _ in range(reps):
+                        torch.matmul(x, w4.dequant(packed, sc, qz, K, g))
+                    e1.record()
+                    torch.cuda.synchronize()
+                    row["naive_dequant_then_matmul_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+                print(json.dumps(row), flush=True)
+                del graph
+            del bufs
+            torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +304,9 @@ def main() -> int:
     ap.add_argument("--m", type=int, default=None, help="rows of x (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a HIP graph")
+    ap.add_argument("--sweep", action="store_true",
+                    help="per-(config, shape, M) timing table of every benchmark config, one JSON "
+                         "line per row, instead of the step benchmark")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (x4), the known-size reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -216,6 +331,9 @@ def main() -> int:
 
     import weight_only_int4_w4a16_amd as w4
     from weight_only_int4_w4a16_amd import synth
+
+    if args.sweep:
+        return sweep(args, torch, w4)
 
     spec = dict(WORKLOADS[args.workload])
     spec["name"] = args.workload

@@ -86,7 +86,8 @@ SMALL = [
     (50, 8192, 32, 128, "f16", "asym"),
     (40, 4160, 48, 64, "bf16", "sym"),
     (20, 8320, 32, 32, "f16", "asym"),
-    # batched kernel (M > 64): ragged M, N not a multiple of the 256-column tile, ragged K,
+    (32, 1024, 48, 64, "bf16", "asym"),
+    # batched kernel (M > 32): ragged M, N not a multiple of the 512-column tile, ragged K,
     # and K long enough to be split across workgroups (K >= 2048)
     (65, 256, 48, 128, "f16", "asym"),
     (128, 384, 272, 32, "f16", "asym"),

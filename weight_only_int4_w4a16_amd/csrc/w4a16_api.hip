@@ -24,13 +24,15 @@ w4a16_status check_shape(int K, int N, int gs) {
 
 w4a16_status from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
-bool use_tiled(const GemmArgs& a) { return a.M > 64 && w4a16::tiled_supported(a); }
+// M above 32 goes to the batched kernel: past two 16-row tiles the decode kernel's
+// activation traffic per weight byte outgrows the batched kernel's dequantization cost
+bool use_tiled(const GemmArgs& a) { return a.M > 32 && w4a16::tiled_supported(a); }
 
 size_t workspace_need(int M, int K, int N, int gs) {
   GemmArgs a{};
   a.M = M; a.K = K; a.N = N; a.group_size = gs;
   if (use_tiled(a)) return w4a16::tiled_workspace_bytes(M, K, N);
-  return w4a16::decode_config(M < 64 ? M : 64, K, N, gs, w4a16::ACT_F16).workspace_bytes;
+  return w4a16::decode_config(M < 32 ? M : 32, K, N, gs, w4a16::ACT_F16).workspace_bytes;
 }
 
 w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
@@ -160,7 +162,7 @@ const char* w4a16_kernel_name(int M, int K, int N, int group_size) {
   GemmArgs a{};
   a.M = M; a.K = K; a.N = N; a.group_size = group_size;
   if (use_tiled(a)) return w4a16::tiled_name(M, K, N);
-  return w4a16::decode_name(M < 64 ? M : 64, K, N, group_size, w4a16::ACT_F16);
+  return w4a16::decode_name(M, K, N, group_size, w4a16::ACT_F16);
 }
 
 const char* w4a16_status_string(w4a16_status s) {

@@ -27,7 +27,7 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
   DecodeConfig c;
   c.KC = ceil_div(K, 128);
   c.NT = N / 16;
-  c.rows = M < 64 ? M : 64;
+  c.rows = M < 32 ? M : 32;
   c.MT = ceil_div(c.rows, 16);
   c.x_in_lds = x_in_lds;
   c.SW = SW;
@@ -50,7 +50,7 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
 // k-block (the register-spill-free instantiations).
 DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
   const int KC = ceil_div(K, 128), NT = N / 16;
-  const int rows = M < 64 ? M : 64, MT = ceil_div(rows, 16);
+  const int rows = M < 32 ? M : 32, MT = ceil_div(rows, 16);
   const int GPC = 128 / group_size;
   const int cus = cu_count();
   const int wmax = decode_block_threads(MT, GPC, x_in_lds) / 64;
@@ -85,7 +85,7 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
 // x goes to LDS when it fits beside the reduction area; otherwise it is read per k-block
 DecodeConfig decode_config(int M, int K, int N, int group_size, int act) {
   (void)act;  // every instantiated configuration exists for both activation types
-  const int rows = M < 64 ? M : 64;
+  const int rows = M < 32 ? M : 32;
   const size_t xbytes = (size_t)rows * ceil_div(K, 128) * 128 * 2;
   if (xbytes <= kXldsBytes) {
     const DecodeConfig c = choose(M, K, N, group_size, true);
@@ -94,23 +94,17 @@ DecodeConfig decode_config(int M, int K, int N, int group_size, int act) {
   return choose(M, K, N, group_size, false);
 }
 
-// Rows of x one launch takes: up to 64 when the activations fit in LDS; with activation
-// fragments held in registers at most 32 (two 16-row tiles), which keeps every
-// instantiation within its registers.
+// Rows of x one launch takes: at most 32 (two 16-row tiles; larger M goes to the batched
+// kernel, and a caller of this launcher with more rows gets several launches).
 DecodeConfig decode_launch_config(int M, int K, int N, int group_size, int act) {
-  const int rows = M < 64 ? M : 64;
-  DecodeConfig c = decode_config(rows, K, N, group_size, act);
-  if (!c.x_in_lds && rows > 32) c = decode_config(32, K, N, group_size, act);
-  return c;
+  return decode_config(M < 32 ? M : 32, K, N, group_size, act);
 }
 
 const char* decode_name(int M, int K, int N, int group_size, int act) {
-  static const char* names[3][3] = {
-      {"w4a16_decode_mt1_sw1", "w4a16_decode_mt1_sw2", "w4a16_decode_mt1_sw4"},
-      {"w4a16_decode_mt2_sw1", "w4a16_decode_mt2_sw2", "w4a16_decode_mt2_sw4"},
-      {"w4a16_decode_mt4_sw1", "w4a16_decode_mt4_sw2", "w4a16_decode_mt4_sw4"}};
+  static const char* names[2][2] = {{"w4a16_decode_mt1_sw1", "w4a16_decode_mt1_sw2"},
+                                    {"w4a16_decode_mt2_sw1", "w4a16_decode_mt2_sw2"}};
   const DecodeConfig c = decode_launch_config(M, K, N, group_size, act);
-  return names[c.MT == 1 ? 0 : c.MT == 2 ? 1 : 2][c.SW == 1 ? 0 : c.SW == 2 ? 1 : 2];
+  return names[c.MT == 1 ? 0 : 1][c.SW == 1 ? 0 : 1];
 }
 
 hipError_t launch_decode(const GemmArgs& a) {

@@ -1,4 +1,4 @@
-// w4a16_decode_kernel.hpp - memory-bound W4A16 GEMM for small M (decode): up to 64 rows per launch.
+// w4a16_decode_kernel.hpp - memory-bound W4A16 GEMM for small M (decode): up to 32 rows per launch.
 //
 // "INT8 vs INT4 Quantization, in depth", section "Two regimes": at small batch a linear
 // layer waits on weight bytes, so this kernel's job is to stream the packed codes once at
@@ -70,10 +70,10 @@ constexpr int decode_block_threads(int MT, int GPC, bool XL) {
   return MT == 1 && GPC <= 2 && XL ? 1024 : 512;
 }
 
-// fp16 affine formats with at most two 16-row tiles multiply integer-valued operands and
+// fp16 affine formats multiply integer-valued operands and
 // apply the group scale to the fp32 partial sums; otherwise W_hat is formed in registers
 // with its one rounding to the activation type.
-constexpr bool decode_defers_scale(int ACT, int FMT, int MT) { return ACT == 0 && FMT != 2 && MT <= 2; }
+constexpr bool decode_defers_scale(int ACT, int FMT) { return ACT == 0 && FMT != 2; }
 
 // workgroup -> tile: tiles [start(x), start(x) + count(x)) run on XCD x = blockIdx % 8
 __device__ __forceinline__ int tile_of(int b, int G) {
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   constexpr int D = XL ? 4 / SW : 1;  // k-blocks per group
   constexpr int SPG = 4 / GPC;        // 32-k steps per scale group
   constexpr bool ZEROS = FMT == FMT_ASYM;
-  constexpr bool DEFER = decode_defers_scale(ACT, FMT, MT);
+  constexpr bool DEFER = decode_defers_scale(ACT, FMT);
 
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
@@ -373,8 +373,7 @@ hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStre
                                    : decode_dispatch_gpc<ACT, FMT, 1, false>(p, c, s);
   if (c.MT == 2) return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 2, true>(p, c, s)
                                    : decode_dispatch_gpc<ACT, FMT, 2, false>(p, c, s);
-  // four 16-row tiles only with x in LDS (launches take at most 32 rows otherwise)
-  return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 4, true>(p, c, s) : hipErrorNotSupported;
+  return hipErrorNotSupported;  // launches take at most 32 rows
 }
 
 }  // namespace w4a16
