@@ -71,7 +71,10 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
       if (wg_per_cu < 1) wg_per_cu = 1;
       const long rounds = ceil_div(c.tiles, cus * wg_per_cu);
       const long cost = rounds * (ceil_div(c.slice, D) + 2);
-      if (best_cost < 0 || cost < best_cost) {
+      // ties: the choice that keeps more compute units busy
+      const int busy = c.tiles < cus ? c.tiles : cus;
+      const int best_busy = best.tiles < cus ? best.tiles : cus;
+      if (best_cost < 0 || cost < best_cost || (cost == best_cost && busy > best_busy)) {
         best = c;
         best_cost = cost;
       }
