@@ -208,6 +208,10 @@ for M in (1, 2, 4, 8, 16, 32, 64, 128, 256):                                # cr
 FULL.append((2048, 8192, 28672, 128, "bf16", "asym"))                       # prefill-shaped
 
 
+# the 128x512 tile with a ragged M, K and N (3 x 87 tiles: enough to be chosen)
+FULL.append((257, 2080, 44048, 32, "f16", "asym"))
+
+
 @pytest.mark.parametrize("M,K,N,g,act,fmt", FULL)
 def test_full_size_sampled_strips(M, K, N, g, act, fmt):
     import weight_only_int4_w4a16_amd as w4

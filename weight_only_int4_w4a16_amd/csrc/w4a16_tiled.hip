@@ -6,7 +6,8 @@
 // rows; "INT4 and Low-Bit Inference", section 5 (Marlin): the unpack is fused into the
 // tile loop and the 16-bit weight tile never goes to HBM.
 //
-// Tiling. A workgroup of eight waves (two per SIMD) computes a 128 x 512 output tile. Each wave owns 64
+// Tiling. A workgroup of eight waves (two per SIMD) computes a 128 x 512 output tile (or, when
+// those tiles would not cover the compute units, four waves a 64 x 256 tile). Each wave owns 64
 // columns (two 32-column pairs of strips) over all 128 rows and multiplies with
 // v_mfma_f32_32x32x16_{f16,bf16}, which on gfx950 delivers twice the flops per cycle of the
 // 16x16x32 form. Its B operand gives lane l column l%32 of a pair and k = 8(l/32) + i of a
@@ -29,16 +30,25 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kBM = 128;            // rows per workgroup tile
 constexpr int kPairs = 2;           // 32-column strip pairs per wave (4 strips of 16)
 constexpr int kStrips = 2 * kPairs;
-constexpr int kWaves = 8;           // waves per workgroup (two per SIMD)
-constexpr int kBN = 16 * kStrips * kWaves;  // 512 columns per workgroup tile
-constexpr int kMT = kBM / 32;       // 32-row MFMA tiles per wave
 constexpr int kAStride = 128 + 8;   // LDS row stride of the activation tile (halves)
-constexpr int kThreads = 64 * kWaves;
-constexpr int kAChunks = kBM * 16 / kThreads;  // 16-byte chunks per thread per k-block
-constexpr size_t kLdsBytes = 2 * kBM * kAStride * 2;  // double-buffered activation tile
+
+// Workgroup tile: MT 32-row MFMA tiles (kBM = 32 MT rows) by WAVES waves of 64 columns.
+// Large: 128 x 512, eight waves (two per SIMD). Small: 64 x 256, four waves, for GEMMs whose
+// large tiles would leave compute units idle (each large tile row of M <= 256 is 28-56
+// tiles at N = 14336).
+template <int MT, int WAVES>
+struct TileShape {
+  static constexpr int kMT = MT;
+  static constexpr int kBM = 32 * MT;
+  static constexpr int kWaves = WAVES;
+  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int kAChunks = kBM * 16 / kThreads;  // 16-byte chunks per thread per block
+  static constexpr size_t kLdsBytes = 2 * kBM * kAStride * 2;  // double-buffered activations
+};
+typedef TileShape<4, 8> LargeTile;
+typedef TileShape<2, 4> SmallTile;
 
 enum Fmt { FMT_ASYM = 0, FMT_SYM = 1, FMT_NF4 = 2 };
 
@@ -70,8 +80,10 @@ __device__ __forceinline__ int tile_of(int b, int G) {
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
-template <int ACT, int GPC, int FMT>
-__global__ __launch_bounds__(kThreads) void tiled_kernel(TiledParams p) {
+template <int ACT, int GPC, int FMT, class T>
+__global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
+  constexpr int kMT = T::kMT, kBM = T::kBM, kWaves = T::kWaves, kThreads = T::kThreads;
+  constexpr int kAChunks = T::kAChunks;
   typedef typename ActT<ACT>::type AT;
   constexpr int SPG = 4 / GPC;
   constexpr bool ZEROS = FMT == FMT_ASYM;
@@ -260,45 +272,57 @@ int cu_count_tiled() {
 }
 
 struct TiledGeometry {
+  bool small;          // SmallTile instead of LargeTile
+  int bm, bn;          // tile rows and columns
   int tiles_m, tiles_n, S, kps;
   size_t partial_bytes;
 };
 
+// Tile: the large one when its tiles alone cover the compute units, else the small one.
 // K slices: double S while the workgroups (tiles x slices) still fit one per compute unit,
 // keeping at least 8 k-blocks per slice.
 TiledGeometry tiled_geometry(int M, int K, int N) {
   TiledGeometry g;
   const int KC = ceil_div(K, 128);
-  g.tiles_m = ceil_div(M, kBM);
-  g.tiles_n = ceil_div(N / 16, kWaves * kStrips);
-  const int tiles = g.tiles_m * g.tiles_n;
   const int cus = cu_count_tiled();
+  const int large = ceil_div(M, LargeTile::kBM) * ceil_div(N / 16, LargeTile::kWaves * kStrips);
+  g.small = large < cus;
+  g.bm = g.small ? SmallTile::kBM : LargeTile::kBM;
+  g.bn = 16 * kStrips * (g.small ? SmallTile::kWaves : LargeTile::kWaves);
+  g.tiles_m = ceil_div(M, g.bm);
+  g.tiles_n = ceil_div(N, g.bn);
+  const int tiles = g.tiles_m * g.tiles_n;
   int S = 1;
   while (tiles * S * 2 <= cus && KC / (2 * S) >= 8) S *= 2;
   g.kps = ceil_div(KC, S);
   g.S = ceil_div(KC, g.kps);
-  g.partial_bytes = g.S > 1 ? (size_t)g.S * g.tiles_m * kBM * N * 4 : 0;
+  g.partial_bytes = g.S > 1 ? (size_t)g.S * g.tiles_m * g.bm * N * 4 : 0;
   return g;
 }
 
-template <int ACT, int GPC>
+template <int ACT, int GPC, class T>
 hipError_t launch_fmt(const GemmArgs& a, const TiledParams& p, dim3 grid) {
   if (a.nf4)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4>), grid, dim3(kThreads), kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4, T>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   else if (a.qzeros)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM>), grid, dim3(kThreads), kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   else
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM>), grid, dim3(kThreads), kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   return hipGetLastError();
 }
 
-template <int ACT>
+template <int ACT, class T>
 hipError_t launch_gpc(const GemmArgs& a, const TiledParams& p, dim3 grid) {
   switch (a.group_size) {
-    case 128: return launch_fmt<ACT, 1>(a, p, grid);
-    case 64: return launch_fmt<ACT, 2>(a, p, grid);
-    default: return launch_fmt<ACT, 4>(a, p, grid);
+    case 128: return launch_fmt<ACT, 1, T>(a, p, grid);
+    case 64: return launch_fmt<ACT, 2, T>(a, p, grid);
+    default: return launch_fmt<ACT, 4, T>(a, p, grid);
   }
+}
+
+template <class T>
+hipError_t launch_act(const GemmArgs& a, const TiledParams& p, dim3 grid) {
+  return a.act == ACT_F16 ? launch_gpc<ACT_F16, T>(a, p, grid) : launch_gpc<ACT_BF16, T>(a, p, grid);
 }
 
 }  // namespace
@@ -306,7 +330,9 @@ hipError_t launch_gpc(const GemmArgs& a, const TiledParams& p, dim3 grid) {
 bool tiled_supported(const GemmArgs&) { return true; }
 
 const char* tiled_name(int M, int K, int N) {
-  return tiled_geometry(M, K, N).S > 1 ? "w4a16_tiled_128x512_splitk" : "w4a16_tiled_128x512";
+  const TiledGeometry g = tiled_geometry(M, K, N);
+  if (g.small) return g.S > 1 ? "w4a16_tiled_64x256_splitk" : "w4a16_tiled_64x256";
+  return g.S > 1 ? "w4a16_tiled_128x512_splitk" : "w4a16_tiled_128x512";
 }
 
 size_t tiled_workspace_bytes(int M, int K, int N) {
@@ -336,11 +362,11 @@ hipError_t launch_tiled(const GemmArgs& a) {
   p.kps = g.kps;
   p.partials = g.S > 1 ? static_cast<float*>(a.workspace) : nullptr;
   const dim3 grid(g.tiles_m * g.tiles_n, g.S);
-  const hipError_t e = a.act == ACT_F16 ? launch_gpc<ACT_F16>(a, p, grid) : launch_gpc<ACT_BF16>(a, p, grid);
+  const hipError_t e = g.small ? launch_act<SmallTile>(a, p, grid) : launch_act<LargeTile>(a, p, grid);
   if (e != hipSuccess || g.S == 1) return e;
   const size_t quads = (size_t)a.M * a.N / 4;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, a.stream,
-                     p.partials, a.M, a.N, g.S, (size_t)g.tiles_m * kBM * a.N, a.out, a.out_dtype);
+                     p.partials, a.M, a.N, g.S, (size_t)g.tiles_m * g.bm * a.N, a.out, a.out_dtype);
   return hipGetLastError();
 }
 
