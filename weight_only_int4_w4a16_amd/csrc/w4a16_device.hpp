@@ -164,9 +164,11 @@ __device__ inline ZeroF32 make_zero_f32(uint32_t z, float s) {
 
 __device__ inline b8_t dequant_word_bf16(uint32_t w, ZeroF32 zs) {
   // device nibble p holds code perm[p]; lo bytes = nibbles 0,2,4,6 = codes 0,4,1,5;
-  // hi bytes = nibbles 1,3,5,7 = codes 2,6,3,7
-  const uint32_t lo = w & 0x0F0F0F0Fu;
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  // hi bytes = nibbles 1,3,5,7 = codes 2,6,3,7. The masks go through v_bitop3 so the
+  // compiler does not narrow each byte to 4 bits, which would cost a shift and an and per
+  // code instead of one v_cvt_f32_ubyte{0,1,2,3} each.
+  const uint32_t lo = and_or(w, 0x0F0F0F0Fu, 0u);
+  const uint32_t hi = and_or(w >> 4, 0x0F0F0F0Fu, 0u);
   float q[8];
   q[0] = (float)(lo & 0xFFu);
   q[4] = (float)((lo >> 8) & 0xFFu);
