@@ -145,42 +145,40 @@ __device__ inline b8_t neg_bias_bf16(uint32_t z) {
 // ---------------------------------------------------------------------------------------
 // bf16 dequantization of one packed word: W_hat = RN_bf16((q - z) * s).
 //
-// Codes are spread into bytes and converted with v_cvt_f32_ubyte*. In fp32,
-// fma(q, s, -(z*s)) is exact: z*s and (q - z)*s are products of a 4/5-bit integer and an
-// 8-bit significand, so both are representable and the fused result needs no rounding.
-// The single rounding is the fp32 -> bf16 conversion (nearest-even).
+// q - z is formed exactly in fp16 (as for the fp16 path), multiplied by s in fp32, where
+// the product of a 5-bit integer and an 8-bit significand is exact, and rounded once by the
+// fp32 -> bf16 conversion (nearest-even).
 // ---------------------------------------------------------------------------------------
 struct ZeroF32 {
-  float s;
-  float nzs;  // -(z * s), exact
+  float s;     // the group scale
+  uint32_t z;  // the 4-bit zero-point
 };
 
 __device__ inline ZeroF32 make_zero_f32(uint32_t z, float s) {
   ZeroF32 r;
   r.s = s;
-  r.nzs = -((float)z * s);
+  r.z = z;
   return r;
 }
 
 __device__ inline b8_t dequant_word_bf16(uint32_t w, ZeroF32 zs) {
-  // device nibble p holds code perm[p]; lo bytes = nibbles 0,2,4,6 = codes 0,4,1,5;
-  // hi bytes = nibbles 1,3,5,7 = codes 2,6,3,7. The masks go through v_bitop3 so the
-  // compiler does not narrow each byte to 4 bits, which would cost a shift and an and per
-  // code instead of one v_cvt_f32_ubyte{0,1,2,3} each.
-  const uint32_t lo = and_or(w, 0x0F0F0F0Fu, 0u);
-  const uint32_t hi = and_or(w >> 4, 0x0F0F0F0Fu, 0u);
-  float q[8];
-  q[0] = (float)(lo & 0xFFu);
-  q[4] = (float)((lo >> 8) & 0xFFu);
-  q[1] = (float)((lo >> 16) & 0xFFu);
-  q[5] = (float)(lo >> 24);
-  q[2] = (float)(hi & 0xFFu);
-  q[6] = (float)((hi >> 8) & 0xFFu);
-  q[3] = (float)((hi >> 16) & 0xFFu);
-  q[7] = (float)(hi >> 24);
+  // q - z exactly, as fp16 pairs, by the magic-number unpack of dequant_word_f16 (codes in
+  // k order); then (q - z) * s exactly in fp32 (5-bit integer times 8-bit significand) and
+  // one round-to-nearest-even to bf16. fma(d, s, +0) equals d * s for every d here (a zero
+  // d is +0), and takes the fp16 d directly (v_fma_mix_f32).
+  const ZeroF16 zc = make_zero_f16(zs.z);
+  const uint32_t w8 = w >> 8;
+  const h2_t d0 = as_h2(and_or(w, 0x000F000Fu, 0x64006400u)) - as_h2(zc.c1024);   // q0, q1
+  const h2_t d1 = as_h2(and_or(w, 0x00F000F0u, 0x54005400u)) - as_h2(zc.c64);     // q2, q3
+  const h2_t d2 = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) - as_h2(zc.c1024);  // q4, q5
+  const h2_t d3 = as_h2(and_or(w8, 0x00F000F0u, 0x54005400u)) - as_h2(zc.c64);    // q6, q7
+  const h2_t d[4] = {d0, d1, d2, d3};
   b8_t r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (__bf16)__builtin_fmaf(q[i], zs.s, zs.nzs);
+  for (int p = 0; p < 4; ++p) {
+    r[2 * p] = (__bf16)__builtin_fmaf((float)d[p][0], zs.s, 0.0f);
+    r[2 * p + 1] = (__bf16)__builtin_fmaf((float)d[p][1], zs.s, 0.0f);
+  }
   return r;
 }
 
