@@ -87,6 +87,11 @@ SMALL = [
     (40, 4160, 48, 64, "bf16", "sym"),
     (20, 8320, 32, 32, "f16", "asym"),
     (32, 1024, 48, 64, "bf16", "asym"),
+    # the smallest shapes: one 32-k step, one 16-column strip
+    (1, 32, 16, 32, "f16", "asym"),
+    (7, 64, 16, 64, "bf16", "sym"),
+    (33, 32, 16, 32, "f16", "asym"),
+    (40, 96, 16, 32, "bf16", "nf4"),
     # batched kernel (M > 32): ragged M, N not a multiple of the 512-column tile, ragged K,
     # and K long enough to be split across workgroups (K >= 2048)
     (65, 256, 48, 128, "f16", "asym"),
