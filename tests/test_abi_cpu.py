@@ -81,12 +81,14 @@ def test_workspace_bytes(L):
     from weight_only_int4_w4a16_amd import workspace_bytes
     assert workspace_bytes(0, 4096, 4096, 128) == 0
     assert workspace_bytes(1, 4096, 4096, 100) == 0
-    for M, K, N in ((1, 4096, 4096), (16, 14336, 4096), (32, 4096, 28672), (1, 352, 48)):
+    for M, K, N in ((1, 4096, 4096), (16, 14336, 4096), (16, 4096, 28672), (1, 352, 48)):
         assert workspace_bytes(M, K, N, 32) == 0    # the decode kernels reduce in LDS
     # batched kernel: no workspace when the output tiles fill the chip, otherwise K is split
-    # and the workspace holds the S fp32 partial tiles (rows padded to the 128-row tile)
+    # and the workspace holds the S fp32 partial tiles (rows padded to the tile's height:
+    # 64 rows for the small tile, chosen when large tiles would not cover the chip)
     assert workspace_bytes(2048, 8192, 28672, 128) == 0
     assert workspace_bytes(200, 2048, 64, 128) == 2 * 256 * 64 * 4
+    assert workspace_bytes(32, 4096, 28672, 128) == 2 * 64 * 28672 * 4
 
 
 def test_nf4_requires_codebook(L):
@@ -110,6 +112,8 @@ def test_kernel_name_and_strings(L):
     from weight_only_int4_w4a16_amd import kernel_name, version
     assert kernel_name(1, 4096, 4096, 128).startswith("w4a16_decode")
     assert kernel_name(0, 4096, 4096, 128) == "none"
+    assert kernel_name(16, 4096, 4096, 128).startswith("w4a16_decode")
+    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_tiled")
     assert kernel_name(65, 4096, 4096, 128).startswith("w4a16_tiled")
     for s in range(5):
         assert L.w4a16_status_string(s)

@@ -82,17 +82,23 @@ SMALL = [
     (12, 448, 48, 64, "f16", "nf4"),
     (2, 256, 32, 64, "bf16", "nf4"),
     (70, 256, 32, 64, "f16", "nf4"),
-    # decode launches with activations too large for LDS (at most 32 rows per launch)
-    (50, 8192, 32, 128, "f16", "asym"),
-    (40, 4160, 48, 64, "bf16", "sym"),
-    (20, 8320, 32, 32, "f16", "asym"),
+    # decode launches with activations too large for LDS (16 rows of 8192 k: 256 KiB)
+    (16, 8192, 32, 128, "f16", "asym"),
+    (9, 4224, 48, 64, "bf16", "sym"),
+    (16, 8320, 32, 32, "f16", "asym"),
+    (16, 1024, 48, 64, "bf16", "asym"),
+    # just past the decode kernel: one ragged 64-row tile of the batched kernel
+    (17, 512, 64, 128, "bf16", "asym"),
     (32, 1024, 48, 64, "bf16", "asym"),
+    (20, 8320, 32, 32, "f16", "asym"),
+    (50, 8192, 32, 128, "f16", "asym"),
     # the smallest shapes: one 32-k step, one 16-column strip
     (1, 32, 16, 32, "f16", "asym"),
     (7, 64, 16, 64, "bf16", "sym"),
     (33, 32, 16, 32, "f16", "asym"),
+    (17, 32, 16, 32, "f16", "sym"),
     (40, 96, 16, 32, "bf16", "nf4"),
-    # batched kernel (M > 32): ragged M, N not a multiple of the 512-column tile, ragged K,
+    # batched kernel (M > 16): ragged M, N not a multiple of the 512-column tile, ragged K,
     # and K long enough to be split across workgroups (K >= 2048)
     (65, 256, 48, 128, "f16", "asym"),
     (128, 384, 272, 32, "f16", "asym"),

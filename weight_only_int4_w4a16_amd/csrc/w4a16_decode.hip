@@ -27,7 +27,7 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
   DecodeConfig c;
   c.KC = ceil_div(K, 128);
   c.NT = N / 16;
-  c.rows = M < 32 ? M : 32;
+  c.rows = M < 16 ? M : 16;
   c.MT = ceil_div(c.rows, 16);
   c.x_in_lds = x_in_lds;
   c.SW = SW;
@@ -50,7 +50,7 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
 // k-block (the register-spill-free instantiations).
 DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
   const int KC = ceil_div(K, 128), NT = N / 16;
-  const int rows = M < 32 ? M : 32, MT = ceil_div(rows, 16);
+  const int rows = M < 16 ? M : 16, MT = ceil_div(rows, 16);
   const int GPC = 128 / group_size;
   const int cus = cu_count();
   const int wmax = decode_block_threads(MT, GPC, x_in_lds) / 64;
@@ -60,7 +60,7 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
   for (int SW = 2; SW >= 1; SW >>= 1) {
     if (NT % SW) continue;
     if (SW > 1 && !(x_in_lds && MT == 1 && GPC == 1)) continue;
-    const int D = x_in_lds ? 4 / SW : 1;  // k-blocks per pipeline group
+    const int D = decode_group_blocks(SW, GPC, x_in_lds);  // k-blocks per pipeline group
     for (int W = wmax; W >= 1; W >>= 1) {
       if (W > 1 && W > KC / D) continue;  // every wave streams at least one whole group
       const DecodeConfig c = geometry(M, K, N, x_in_lds, SW, W);
@@ -88,7 +88,7 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
 // x goes to LDS when it fits beside the reduction area; otherwise it is read per k-block
 DecodeConfig decode_config(int M, int K, int N, int group_size, int act) {
   (void)act;  // every instantiated configuration exists for both activation types
-  const int rows = M < 32 ? M : 32;
+  const int rows = M < 16 ? M : 16;
   const size_t xbytes = (size_t)rows * ceil_div(K, 128) * 128 * 2;
   if (xbytes <= kXldsBytes) {
     const DecodeConfig c = choose(M, K, N, group_size, true);
@@ -97,17 +97,15 @@ DecodeConfig decode_config(int M, int K, int N, int group_size, int act) {
   return choose(M, K, N, group_size, false);
 }
 
-// Rows of x one launch takes: at most 32 (two 16-row tiles; larger M goes to the batched
-// kernel, and a caller of this launcher with more rows gets several launches).
+// Rows of x one launch takes: at most 16, one MFMA tile (larger M goes to the batched
+// kernel; a caller of this launcher with more rows gets several launches).
 DecodeConfig decode_launch_config(int M, int K, int N, int group_size, int act) {
-  return decode_config(M < 32 ? M : 32, K, N, group_size, act);
+  return decode_config(M < 16 ? M : 16, K, N, group_size, act);
 }
 
 const char* decode_name(int M, int K, int N, int group_size, int act) {
-  static const char* names[2][2] = {{"w4a16_decode_mt1_sw1", "w4a16_decode_mt1_sw2"},
-                                    {"w4a16_decode_mt2_sw1", "w4a16_decode_mt2_sw2"}};
   const DecodeConfig c = decode_launch_config(M, K, N, group_size, act);
-  return names[c.MT == 1 ? 0 : 1][c.SW == 1 ? 0 : 1];
+  return c.SW == 1 ? "w4a16_decode_sw1" : "w4a16_decode_sw2";
 }
 
 hipError_t launch_decode(const GemmArgs& a) {

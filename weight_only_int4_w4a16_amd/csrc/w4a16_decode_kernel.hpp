@@ -1,4 +1,4 @@
-// w4a16_decode_kernel.hpp - memory-bound W4A16 GEMM for small M (decode): up to 32 rows per launch.
+// w4a16_decode_kernel.hpp - memory-bound W4A16 GEMM for small M (decode): up to 16 rows per launch.
 //
 // "INT8 vs INT4 Quantization, in depth", section "Two regimes": at small batch a linear
 // layer waits on weight bytes, so this kernel's job is to stream the packed codes once at
@@ -64,10 +64,17 @@ struct DecodeParams {
 constexpr int kXRegs = 2;  // 16-byte chunks of x per lane staged in registers ahead of the weights
 
 // Largest workgroup of an instantiation, 1024 or 512 threads. 1024 caps a lane at 128
-// registers (4 waves per SIMD); instantiations that need more (several 16-row tiles, four
-// scale groups per k-block, or activation fragments held in registers) get 512.
+// registers (4 waves per SIMD); instantiations that need more (two 16-row tiles, or
+// activation fragments held in registers) get 512.
 constexpr int decode_block_threads(int MT, int GPC, bool XL) {
-  return MT == 1 && GPC <= 2 && XL ? 1024 : 512;
+  return MT == 1 && XL ? 1024 : 512;
+}
+
+// k-blocks per pipeline group: four blocks (4 KiB) per group with x in LDS, halved for four
+// scale groups per block (their scales and zero words would not fit the 128 registers of a
+// 1024-thread workgroup); one block when the activation fragments travel with the codes.
+constexpr int decode_group_blocks(int SW, int GPC, bool XL) {
+  return XL ? (GPC == 4 ? 2 : 4) / SW : 1;
 }
 
 // fp16 affine formats multiply integer-valued operands and
@@ -84,7 +91,7 @@ __device__ __forceinline__ int tile_of(int b, int G) {
 template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, int LB>
 __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   typedef typename ActT<ACT>::type AT;
-  constexpr int D = XL ? 4 / SW : 1;  // k-blocks per group
+  constexpr int D = decode_group_blocks(SW, GPC, XL);  // k-blocks per group
   constexpr int SPG = 4 / GPC;        // 32-k steps per scale group
   constexpr bool ZEROS = FMT == FMT_ASYM;
   constexpr bool DEFER = decode_defers_scale(ACT, FMT);
@@ -371,9 +378,7 @@ template <int ACT, int FMT>
 hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
   if (c.MT == 1) return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 1, true>(p, c, s)
                                    : decode_dispatch_gpc<ACT, FMT, 1, false>(p, c, s);
-  if (c.MT == 2) return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 2, true>(p, c, s)
-                                   : decode_dispatch_gpc<ACT, FMT, 2, false>(p, c, s);
-  return hipErrorNotSupported;  // launches take at most 32 rows
+  return hipErrorNotSupported;  // launches take at most 16 rows
 }
 
 }  // namespace w4a16

@@ -25,7 +25,7 @@ struct GemmArgs {
   hipStream_t stream;
 };
 
-// launch geometry of the decode kernel (at most 32 rows of x per launch)
+// launch geometry of the decode kernel (at most 16 rows of x per launch)
 struct DecodeConfig {
   int KC, NT;        // k-blocks per strip, 16-column strips
   int rows, MT;      // rows of x, 16-row MFMA tiles
@@ -45,8 +45,8 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 hipError_t launch_pack(const uint32_t* qweight, int K, int N, uint32_t* packed, hipStream_t s);
 hipError_t launch_dequant(const GemmArgs& a);  // writes W_hat [K][N] into a.out (act dtype)
-hipError_t launch_decode(const GemmArgs& a);   // M <= 32 (more rows: several launches)
-hipError_t launch_tiled(const GemmArgs& a);    // M > 32
+hipError_t launch_decode(const GemmArgs& a);   // M <= 16 (more rows: several launches)
+hipError_t launch_tiled(const GemmArgs& a);    // M > 16
 size_t tiled_workspace_bytes(int M, int K, int N);
 const char* decode_name(int M, int K, int N, int group_size, int act);
 const char* tiled_name(int M, int K, int N);

@@ -1,4 +1,4 @@
-// w4a16_tiled.hip - W4A16 GEMM for batched and prefill shapes (M > 32), where the MFMAs and
+// w4a16_tiled.hip - W4A16 GEMM for batched and prefill shapes (M > 16), where the MFMAs and
 // not the weight bytes bound the time.
 //
 // "INT8 vs INT4 Quantization, in depth", section "Two regimes": past the crossover batch a
