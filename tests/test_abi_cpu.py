@@ -115,6 +115,11 @@ def test_kernel_name_and_strings(L):
     assert kernel_name(16, 4096, 4096, 128).startswith("w4a16_decode")
     assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_tiled")
     assert kernel_name(65, 4096, 4096, 128).startswith("w4a16_tiled")
+    # the ragged full-size parity shapes land on each batched geometry (256 compute units)
+    assert kernel_name(257, 2080, 44048, 32) == "w4a16_tiled_64x256"
+    assert kernel_name(513, 2080, 44048, 32) == "w4a16_tiled_128x512"
+    assert kernel_name(129, 4224, 28688, 64) == "w4a16_tiled_128x512_splitk"
+    assert kernel_name(2048, 8192, 28672, 128) == "w4a16_tiled_128x512"
     for s in range(5):
         assert L.w4a16_status_string(s)
     assert version()

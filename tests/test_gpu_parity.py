@@ -219,8 +219,11 @@ for M in (1, 2, 4, 8, 16, 32, 64, 128, 256):                                # cr
 FULL.append((2048, 8192, 28672, 128, "bf16", "asym"))                       # prefill-shaped
 
 
-# the 128x512 tile with a ragged M, K and N (3 x 87 tiles: enough to be chosen)
+# ragged M, K and N on each batched geometry (test_abi_cpu pins which one a shape gets):
+# 64x256 tiles, 128x512 tiles, and 128x512 tiles with K split in two
 FULL.append((257, 2080, 44048, 32, "f16", "asym"))
+FULL.append((513, 2080, 44048, 32, "f16", "asym"))
+FULL.append((129, 4224, 28688, 64, "bf16", "asym"))
 
 
 @pytest.mark.parametrize("M,K,N,g,act,fmt", FULL)

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
           const int m = m0 + mt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
           if (p.S == 1) {
             if (m < M) store_out(p.out, (size_t)m * N + col, acc[mt][pr][i], p.out_dtype);
-          } else {
+          } else if (m < M) {
             // K split: this slice's fp32 partial tile; the reduce kernel sums the slices
             p.partials[z * slice_stride + (size_t)m * N + col] = acc[mt][pr][i];
           }
@@ -278,17 +278,14 @@ struct TiledGeometry {
   size_t partial_bytes;
 };
 
-// Tile: the large one when its tiles alone cover the compute units, else the small one.
 // K slices: double S while the workgroups (tiles x slices) still fit one per compute unit,
 // keeping at least 8 k-blocks per slice.
-TiledGeometry tiled_geometry(int M, int K, int N) {
+TiledGeometry geometry_for(int M, int K, int N, bool small, int cus) {
   TiledGeometry g;
   const int KC = ceil_div(K, 128);
-  const int cus = cu_count_tiled();
-  const int large = ceil_div(M, LargeTile::kBM) * ceil_div(N / 16, LargeTile::kWaves * kStrips);
-  g.small = large < cus;
-  g.bm = g.small ? SmallTile::kBM : LargeTile::kBM;
-  g.bn = 16 * kStrips * (g.small ? SmallTile::kWaves : LargeTile::kWaves);
+  g.small = small;
+  g.bm = small ? SmallTile::kBM : LargeTile::kBM;
+  g.bn = 16 * kStrips * (small ? SmallTile::kWaves : LargeTile::kWaves);
   g.tiles_m = ceil_div(M, g.bm);
   g.tiles_n = ceil_div(N, g.bn);
   const int tiles = g.tiles_m * g.tiles_n;
@@ -298,6 +295,32 @@ TiledGeometry tiled_geometry(int M, int K, int N) {
   g.S = ceil_div(KC, g.kps);
   g.partial_bytes = g.S > 1 ? (size_t)g.S * g.tiles_m * g.bm * N * 4 : 0;
   return g;
+}
+
+// Modelled time of a geometry: the busiest compute unit's tile flops (padded rows included)
+// at the rate one compute unit sustains with that tile, plus, when K is split, the fp32
+// partial sums written and read back at 5 TB/s and the reduce launch. Rates measured on
+// MI355X (fp16, g128): large tile 4.2-5.4 TFLOP/s per compute unit (4.6 taken); small tile
+// 2.7 with one workgroup per compute unit, 3.4 with two or more.
+double modelled_us(const TiledGeometry& g, int M, int N, int cus) {
+  const long wgs = (long)g.tiles_m * g.tiles_n * g.S;
+  const long per_cu = (wgs + cus - 1) / cus;
+  const double wg_flops = 2.0 * g.bm * g.bn * g.kps * 128;
+  const double rate = !g.small ? 4.6e6 : per_cu > 1 ? 3.4e6 : 2.7e6;  // flop per us
+  double us = per_cu * wg_flops / rate;
+  if (g.S > 1) us += 2.0 * g.S * M * (double)N * 4 / 5e6 + 2.0;
+  return us;
+}
+
+// Tile: the large one (each dequantized word feeds four 32-row tiles, not two) or the small
+// one (more workgroups), whichever the model above makes faster. It tracks the measured
+// choice: large wins by 12-21% at 8192x28672 M=256, 28672x8192 M=256, 8192x10240 M=512 and
+// loses by 7-13% at 4096x4096 M=512 and 1024 (split-K partials outweigh its rate).
+TiledGeometry tiled_geometry(int M, int K, int N) {
+  const int cus = cu_count_tiled();
+  const TiledGeometry large = geometry_for(M, K, N, false, cus);
+  const TiledGeometry small = geometry_for(M, K, N, true, cus);
+  return modelled_us(large, M, N, cus) < modelled_us(small, M, N, cus) ? large : small;
 }
 
 template <int ACT, int GPC, class T>
