@@ -391,7 +391,8 @@ def main() -> int:
     per_shape = []
     for si, (K, N) in enumerate(spec["shapes"]):
         r = capture(make_step(spec, layers, xs, ys, codebook, w4, only=si))
-        r()
+        for _ in range(max(1, args.warmup)):
+            r()
         us = timed(r, args.steps) * 1e3 / (args.steps * spec["layers"])
         b = algo_bytes(M, K, N, spec["g"], zeros, nf4)
         per_shape.append({"linear": spec["names"][si], "K": K, "N": N,
