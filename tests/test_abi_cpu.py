@@ -87,7 +87,7 @@ def test_workspace_bytes(L):
     # and the workspace holds the S fp32 partial tiles (rows padded to the tile's height:
     # 64 rows for the small tile, chosen when large tiles would not cover the chip)
     assert workspace_bytes(2048, 8192, 28672, 128) == 0
-    assert workspace_bytes(200, 2048, 64, 128) == 2 * 256 * 64 * 4
+    assert workspace_bytes(200, 2048, 64, 128) == 8 * 256 * 64 * 4    # 8 slices of 2 k-blocks
     assert workspace_bytes(32, 4096, 28672, 128) == 2 * 64 * 28672 * 4
 
 

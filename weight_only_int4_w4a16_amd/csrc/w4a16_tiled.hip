@@ -278,9 +278,8 @@ struct TiledGeometry {
   size_t partial_bytes;
 };
 
-// K slices: double S while the workgroups (tiles x slices) still fit one per compute unit,
-// keeping at least 8 k-blocks per slice.
-TiledGeometry geometry_for(int M, int K, int N, bool small, int cus) {
+// A tile kind with K cut into (about) S contiguous slices of whole k-blocks.
+TiledGeometry geometry_for(int M, int K, int N, bool small, int S) {
   TiledGeometry g;
   const int KC = ceil_div(K, 128);
   g.small = small;
@@ -288,39 +287,50 @@ TiledGeometry geometry_for(int M, int K, int N, bool small, int cus) {
   g.bn = 16 * kStrips * (small ? SmallTile::kWaves : LargeTile::kWaves);
   g.tiles_m = ceil_div(M, g.bm);
   g.tiles_n = ceil_div(N, g.bn);
-  const int tiles = g.tiles_m * g.tiles_n;
-  int S = 1;
-  while (tiles * S * 2 <= cus && KC / (2 * S) >= 8) S *= 2;
   g.kps = ceil_div(KC, S);
   g.S = ceil_div(KC, g.kps);
   g.partial_bytes = g.S > 1 ? (size_t)g.S * g.tiles_m * g.bm * N * 4 : 0;
   return g;
 }
 
-// Modelled time of a geometry: the busiest compute unit's tile flops (padded rows included)
-// at the rate one compute unit sustains with that tile, plus, when K is split, the fp32
-// partial sums written and read back at 5 TB/s and the reduce launch. Rates measured on
-// MI355X (fp16, g128): large tile 4.2-5.4 TFLOP/s per compute unit (4.6 taken); small tile
-// 2.7 with one workgroup per compute unit, 3.4 with two or more.
+// Modelled time of a geometry: on the busiest compute unit, each of its workgroups costs a
+// fixed 2.5 us (pipeline fill, epilogue) plus its tile flops (padded rows included) at the
+// rate one compute unit sustains with that tile; when K is split, the fp32 partial sums are
+// written and read back at 5 TB/s and the reduce launch costs 2 us. Rates measured on MI355X
+// (fp16, g128): large tile 4.2-5.4 TFLOP/s per compute unit (4.6 taken); small tile 2.7 with
+// one workgroup per compute unit, 3.4 with two or more.
 double modelled_us(const TiledGeometry& g, int M, int N, int cus) {
   const long wgs = (long)g.tiles_m * g.tiles_n * g.S;
   const long per_cu = (wgs + cus - 1) / cus;
   const double wg_flops = 2.0 * g.bm * g.bn * g.kps * 128;
   const double rate = !g.small ? 4.6e6 : per_cu > 1 ? 3.4e6 : 2.7e6;  // flop per us
-  double us = per_cu * wg_flops / rate;
+  double us = per_cu * (2.5 + wg_flops / rate);
   if (g.S > 1) us += 2.0 * g.S * M * (double)N * 4 / 5e6 + 2.0;
   return us;
 }
 
-// Tile: the large one (each dequantized word feeds four 32-row tiles, not two) or the small
-// one (more workgroups), whichever the model above makes faster. It tracks the measured
-// choice: large wins by 12-21% at 8192x28672 M=256, 28672x8192 M=256, 8192x10240 M=512 and
-// loses by 7-13% at 4096x4096 M=512 and 1024 (split-K partials outweigh its rate).
+// Tile and K split: the large tile (each dequantized word feeds four 32-row tiles, not two)
+// or the small one (more workgroups), each with S = 1, 2, 4, ... slices of at least two
+// k-blocks and at most four workgroups per compute unit; the model's fastest wins. It
+// tracks the measured choices: large wins by 12-21% at 8192x28672 M=256, 28672x8192 M=256,
+// 8192x10240 M=512 and loses by 7-13% at 4096x4096 M=512 and 1024 (split-K partials
+// outweigh its rate); small matrices past 16 rows split K deeply (4096x4096 at M=17: S=16).
 TiledGeometry tiled_geometry(int M, int K, int N) {
   const int cus = cu_count_tiled();
-  const TiledGeometry large = geometry_for(M, K, N, false, cus);
-  const TiledGeometry small = geometry_for(M, K, N, true, cus);
-  return modelled_us(large, M, N, cus) < modelled_us(small, M, N, cus) ? large : small;
+  const int KC = ceil_div(K, 128);
+  TiledGeometry best = geometry_for(M, K, N, true, 1);
+  double best_us = modelled_us(best, M, N, cus);
+  for (int small = 0; small < 2; ++small)
+    for (int S = 1; S == 1 || KC / S >= 2; S *= 2) {
+      const TiledGeometry g = geometry_for(M, K, N, small != 0, S);
+      if (S > 1 && (long)g.tiles_m * g.tiles_n * g.S > 4L * cus) break;
+      const double us = modelled_us(g, M, N, cus);
+      if (us < best_us) {
+        best = g;
+        best_us = us;
+      }
+    }
+  return best;
 }
 
 template <int ACT, int GPC, class T>
