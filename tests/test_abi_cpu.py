@@ -113,6 +113,12 @@ def test_kernel_name_and_strings(L):
     assert kernel_name(1, 4096, 4096, 128).startswith("w4a16_decode")
     assert kernel_name(0, 4096, 4096, 128) == "none"
     assert kernel_name(16, 4096, 4096, 128).startswith("w4a16_decode")
+    # decode parity shapes that run persistent workgroups (256 compute units)
+    for M, K, N, g in ((16, 4096, 9216, 128), (13, 3968, 9248, 128), (12, 4224, 8208, 64),
+                       (15, 2080, 12304, 32), (12, 4096, 8208, 128), (8, 4096, 16400, 32),
+                       (16, 4096, 28672, 128)):
+        assert kernel_name(M, K, N, g).endswith("_persist"), (M, K, N, g)
+    assert not kernel_name(1, 4096, 28672, 128).endswith("_persist")
     assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_tiled")
     assert kernel_name(65, 4096, 4096, 128).startswith("w4a16_tiled")
     # the ragged full-size parity shapes land on each batched geometry (256 compute units)

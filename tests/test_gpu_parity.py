@@ -92,6 +92,14 @@ SMALL = [
     (32, 1024, 48, 64, "bf16", "asym"),
     (20, 8320, 32, 32, "f16", "asym"),
     (50, 8192, 32, 128, "f16", "asym"),
+    # persistent decode workgroups (more tiles than resident slots, x staged once): one and
+    # two strips per tile, waves with one group and with several, a ragged K, g32
+    (16, 4096, 9216, 128, "f16", "asym"),
+    (13, 3968, 9248, 128, "bf16", "asym"),
+    (12, 4224, 8208, 64, "bf16", "sym"),
+    (15, 2080, 12304, 32, "f16", "asym"),
+    (12, 4096, 8208, 128, "f16", "sym"),
+    (8, 4096, 16400, 32, "f16", "asym"),
     # the smallest shapes: one 32-k step, one 16-column strip
     (1, 32, 16, 32, "f16", "asym"),
     (7, 64, 16, 64, "bf16", "sym"),

@@ -32,6 +32,8 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
   c.x_in_lds = x_in_lds;
   c.SW = SW;
   c.tiles = c.NT / SW;
+  c.grid = c.tiles;
+  c.persist = false;
   c.slice = ceil_div(c.KC, W);
   c.W = ceil_div(c.KC, c.slice);  // drop waves left without blocks
   c.xstride = c.slice * 128 + 8;
@@ -48,6 +50,15 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
 // choice wins, wider tiles (shared activation fragments and scale lines) and then more
 // waves on ties. Two-strip tiles exist for x in LDS, one 16-row tile and one scale group per
 // k-block (the register-spill-free instantiations).
+//
+// Persistent workgroups. Every round restages all of x in LDS (rows x K x 2 bytes, against
+// SW x 8 x K bytes of codes per tile), so from 8 rows on, when the best launch above needs
+// more than one round, the workgroups persist instead: 512 threads (up to 256 registers,
+// 8 waves per compute unit), one per resident slot (a multiple of 8), each taking every
+// grid-th tile with x staged once. A tile then costs its groups plus one (the next tile's
+// loads are in flight while the wave partials are summed), the launch one more. Measured:
+// 4096x28672 at M=16 33.5 -> 23.0 us, 8192x57344 at M=8 77.9 -> 54.7 us, 8192x10240 at M=8
+// 21.0 -> 18.2 us; at M=4 the same rule would lose (4096x28672 17.3 -> 20.4 us).
 DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
   const int KC = ceil_div(K, 128), NT = N / 16;
   const int rows = M < 16 ? M : 16, MT = ceil_div(rows, 16);
@@ -55,8 +66,8 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
   const int cus = cu_count();
   const int wmax = decode_block_threads(MT, GPC, x_in_lds) / 64;
   const int waves_per_cu = wmax == 16 ? 16 : 8;
-  DecodeConfig best{};
-  long best_cost = -1;
+  DecodeConfig best{}, pbest{};
+  long best_cost = -1, best_rounds = 0, pbest_cost = -1;
   for (int SW = 2; SW >= 1; SW >>= 1) {
     if (NT % SW) continue;
     if (SW > 1 && !(x_in_lds && MT == 1 && GPC == 1)) continue;
@@ -77,9 +88,26 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
       if (best_cost < 0 || cost < best_cost || (cost == best_cost && busy > best_busy)) {
         best = c;
         best_cost = cost;
+        best_rounds = rounds;
+      }
+      if (x_in_lds && W <= decode_persistent_threads / 64) {
+        int per_cu = 8 / W;
+        if (by_lds < per_cu) per_cu = by_lds;
+        if (per_cu < 1) per_cu = 1;
+        const int grid = cus * per_cu / 8 * 8;
+        if (grid >= 8 && grid < c.tiles) {
+          const long pcost = ceil_div(c.tiles, grid) * (ceil_div(c.slice, D) + 1) + 1;
+          if (pbest_cost < 0 || pcost < pbest_cost) {
+            pbest = c;
+            pbest.grid = grid;
+            pbest.persist = true;
+            pbest_cost = pcost;
+          }
+        }
       }
     }
   }
+  if (rows >= 8 && best_rounds > 1 && pbest_cost >= 0) return pbest;
   return best;
 }
 
@@ -105,6 +133,7 @@ DecodeConfig decode_launch_config(int M, int K, int N, int group_size, int act) 
 
 const char* decode_name(int M, int K, int N, int group_size, int act) {
   const DecodeConfig c = decode_launch_config(M, K, N, group_size, act);
+  if (c.persist) return c.SW == 1 ? "w4a16_decode_sw1_persist" : "w4a16_decode_sw2_persist";
   return c.SW == 1 ? "w4a16_decode_sw1" : "w4a16_decode_sw2";
 }
 

@@ -70,6 +70,10 @@ constexpr int decode_block_threads(int MT, int GPC, bool XL) {
   return MT == 1 && XL ? 1024 : 512;
 }
 
+// Workgroup size of the persistent instantiations: 512 threads, so a lane may hold the next
+// tile's prefetched groups beside the current tile's accumulators (up to 256 registers).
+constexpr int decode_persistent_threads = 512;
+
 // k-blocks per pipeline group: four blocks (4 KiB) per group with x in LDS, halved for four
 // scale groups per block (their scales and zero words would not fit the 128 registers of a
 // 1024-thread workgroup); one block when the activation fragments travel with the codes.
@@ -88,7 +92,9 @@ __device__ __forceinline__ int tile_of(int b, int G) {
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
-template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, int LB>
+// PT (persistent tiles): the grid is smaller than the tile count and each workgroup loops
+// over tiles blockIdx.x, + gridDim.x, ... with x staged once.
+template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, int LB, bool PT>
 __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   typedef typename ActT<ACT>::type AT;
   constexpr int D = decode_group_blocks(SW, GPC, XL);  // k-blocks per group
@@ -99,13 +105,11 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tile = tile_of(blockIdx.x, p.tiles);
   const int K = p.K, N = p.N, KC = p.KC, rows = p.M;
   const int kc0 = min(wave * p.slice, KC);
   const int kc1 = min(kc0 + p.slice, KC);
   const int ng = (kc1 - kc0 + D - 1) / D;  // groups of this wave
-  const int col = tile * SW * 16 + (lane & 15);  // this lane's column in strip 0 of the tile
-  const int shift = 4 * (lane & 7);              // nibble of the column in its zero word
+  const int shift = 4 * (lane & 7);  // nibble of the lane's column in its zero word
 
   float* red = reinterpret_cast<float*>(lds);                                   // [W][SW][rows][16]
   uint16_t* xs = reinterpret_cast<uint16_t*>(red + (size_t)p.W * SW * rows * 16) +
@@ -118,7 +122,8 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   u4_t xA[XL ? 1 : MT][4], xB[XL ? 1 : MT][4];
 
   auto load_group = [&](u4_t(&b)[D][SW], uint16_t(&s)[D][SW][GPC], uint32_t(&z)[D][SW][GPC],
-                        u4_t(&xf)[XL ? 1 : MT][4], int t) {
+                        u4_t(&xf)[XL ? 1 : MT][4], int tile, int t) __attribute__((always_inline)) {
+    const int col = tile * SW * 16 + (lane & 15);  // this lane's column in strip 0 of the tile
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int kc = min(kc0 + t * D + d, kc1 - 1);  // past the slice: reload its last block
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   // full groups take the branch-free copy
   auto compute_group = [&](const u4_t(&b)[D][SW], const uint16_t(&s)[D][SW][GPC],
                            const uint32_t(&z)[D][SW][GPC], const u4_t(&xf)[XL ? 1 : MT][4],
-                           int t, auto guard) {
+                           int t, auto guard) __attribute__((always_inline)) {
     constexpr bool GUARD = decltype(guard)::value;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   const int kfull = K >> 7;  // k-blocks without a ragged tail
   const int kend = kc1 < kfull ? kc1 : kfull;
   auto compute = [&](const u4_t(&b)[D][SW], const uint16_t(&s)[D][SW][GPC],
-                     const uint32_t(&z)[D][SW][GPC], const u4_t(&xf)[XL ? 1 : MT][4], int t) {
+                     const uint32_t(&z)[D][SW][GPC], const u4_t(&xf)[XL ? 1 : MT][4], int t) __attribute__((always_inline)) {
     if (kc0 + (t + 1) * D <= kend) compute_group(b, s, z, xf, t, std::false_type{});
     else compute_group(b, s, z, xf, t, std::true_type{});
   };
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   const int nchunks = XL ? rows * cpr : 0;
   u4_t xr[kXRegs];
   int xoff[kXRegs];
-  auto x_load = [&]() {
+  auto x_load = [&]() __attribute__((always_inline)) {
     if constexpr (XL) {
 #pragma unroll
       for (int i = 0; i < kXRegs; ++i) {
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
       }
     }
   };
-  auto x_store = [&]() {
+  auto x_store = [&]() __attribute__((always_inline)) {
     if constexpr (XL) {
 #pragma unroll
       for (int i = 0; i < kXRegs; ++i) *reinterpret_cast<u4_t*>(xs + xoff[i]) = xr[i];
@@ -289,56 +294,136 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
     }
   };
 
+  // ---- sum the W partial tiles of a tile in wave order and store it ----
+  auto reduce_store = [&](int tile) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mt * 16 + 4 * (lane >> 4) + r;
+          if (m < rows) red[(((size_t)wave * SW + sw) * rows + m) * 16 + (lane & 15)] = acc[sw][mt][r];
+          if constexpr (PT) acc[sw][mt][r] = 0.f;
+        }
+    __syncthreads();
+    const int per_wave = SW * rows * 16;
+    for (int e = threadIdx.x; e < per_wave; e += blockDim.x) {
+      float v = 0.f;
+      for (int w = 0; w < p.W; ++w) v += red[(size_t)w * per_wave + e];
+      const int sw = e / (rows * 16);
+      const int rem = e - sw * rows * 16;
+      const int m = rem >> 4, c = rem & 15;
+      store_out(p.out, (size_t)m * N + (size_t)(tile * SW + sw) * 16 + c, v, p.out_dtype);
+    }
+    if constexpr (PT) __syncthreads();  // the next tile's partials overwrite red
+  };
+
   // Every path below issues its loads unconditionally, so the compiler's wait before each
   // group covers exactly the loads issued before that group's (a load issued on only some
   // paths into a join would make it wait for everything).
-  if (ng == 1) {
-    x_load();
-    load_group(bA, sA, zA, xA, 0);
-    x_store();
-    compute(bA, sA, zA, xA, 0);
-  } else if (ng > 1) {
-    x_load();
-    load_group(bA, sA, zA, xA, 0);
-    load_group(bB, sB, zB, xB, 1);
-    x_store();
-    int t = 0;
-    for (; t + 3 < ng; t += 2) {  // groups t+2 and t+3 exist
-      compute(bA, sA, zA, xA, t);
-      load_group(bA, sA, zA, xA, t + 2);
-      compute(bB, sB, zB, xB, t + 1);
-      load_group(bB, sB, zB, xB, t + 3);
-    }
-    if (t + 2 < ng) {  // three groups left
-      compute(bA, sA, zA, xA, t);
-      load_group(bA, sA, zA, xA, t + 2);
-      compute(bB, sB, zB, xB, t + 1);
-      compute(bA, sA, zA, xA, t + 2);
-    } else {  // two groups left
-      compute(bA, sA, zA, xA, t);
-      compute(bB, sB, zB, xB, t + 1);
-    }
-  }
-
-  // ---- sum the W partial tiles in wave order ----
-#pragma unroll
-  for (int sw = 0; sw < SW; ++sw)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mt * 16 + 4 * (lane >> 4) + r;
-        if (m < rows) red[(((size_t)wave * SW + sw) * rows + m) * 16 + (lane & 15)] = acc[sw][mt][r];
+  if constexpr (!PT) {
+    const int tile = tile_of(blockIdx.x, p.tiles);
+    if (ng == 1) {
+      x_load();
+      load_group(bA, sA, zA, xA, tile, 0);
+      x_store();
+      compute(bA, sA, zA, xA, 0);
+    } else if (ng > 1) {
+      x_load();
+      load_group(bA, sA, zA, xA, tile, 0);
+      load_group(bB, sB, zB, xB, tile, 1);
+      x_store();
+      int t = 0;
+      for (; t + 3 < ng; t += 2) {  // groups t+2 and t+3 exist
+        compute(bA, sA, zA, xA, t);
+        load_group(bA, sA, zA, xA, tile, t + 2);
+        compute(bB, sB, zB, xB, t + 1);
+        load_group(bB, sB, zB, xB, tile, t + 3);
       }
-  __syncthreads();
-  const int per_wave = SW * rows * 16;
-  for (int e = threadIdx.x; e < per_wave; e += blockDim.x) {
-    float v = 0.f;
-    for (int w = 0; w < p.W; ++w) v += red[(size_t)w * per_wave + e];
-    const int sw = e / (rows * 16);
-    const int rem = e - sw * rows * 16;
-    const int m = rem >> 4, c = rem & 15;
-    store_out(p.out, (size_t)m * N + (size_t)(tile * SW + sw) * 16 + c, v, p.out_dtype);
+      if (t + 2 < ng) {  // three groups left
+        compute(bA, sA, zA, xA, t);
+        load_group(bA, sA, zA, xA, tile, t + 2);
+        compute(bB, sB, zB, xB, t + 1);
+        compute(bA, sA, zA, xA, t + 2);
+      } else {  // two groups left
+        compute(bA, sA, zA, xA, t);
+        compute(bB, sB, zB, xB, t + 1);
+      }
+    }
+    reduce_store(tile);
+  } else {
+    // The workgroup's tiles: blockIdx.x, then every gridDim.x-th (a multiple of 8, so the
+    // same XCD). The next tile's first two groups load while the current tile's last
+    // groups are multiplied and its partials summed; waves with a single group run a loop
+    // of their own, and the last tile's tail, which prefetches nothing, is a separate copy
+    // after which the loop exits.
+    auto tile_loop = [&](auto single) __attribute__((always_inline)) {
+      constexpr bool ONE = decltype(single)::value;
+      int bi = blockIdx.x;
+      int tile = tile_of(bi, p.tiles);
+      x_load();
+      load_group(bA, sA, zA, xA, tile, 0);
+      if constexpr (!ONE) load_group(bB, sB, zB, xB, tile, 1);
+      x_store();
+      auto body = [&]() __attribute__((always_inline)) -> int {  // all but the last 2-3 groups
+        int t = 0;
+        for (; t + 3 < ng; t += 2) {
+          compute(bA, sA, zA, xA, t);
+          load_group(bA, sA, zA, xA, tile, t + 2);
+          compute(bB, sB, zB, xB, t + 1);
+          load_group(bB, sB, zB, xB, tile, t + 3);
+        }
+        return t;
+      };
+      for (;;) {
+        const int bn = bi + (int)gridDim.x;
+        if (bn < p.tiles) {
+          const int tn = tile_of(bn, p.tiles);
+          if constexpr (ONE) {
+            compute(bA, sA, zA, xA, 0);
+            load_group(bA, sA, zA, xA, tn, 0);
+          } else {
+            const int t = body();
+            if (t + 2 < ng) {
+              compute(bA, sA, zA, xA, t);
+              load_group(bA, sA, zA, xA, tile, t + 2);
+              compute(bB, sB, zB, xB, t + 1);
+              compute(bA, sA, zA, xA, t + 2);
+              load_group(bA, sA, zA, xA, tn, 0);
+              load_group(bB, sB, zB, xB, tn, 1);
+            } else {
+              compute(bA, sA, zA, xA, t);
+              load_group(bA, sA, zA, xA, tn, 0);
+              compute(bB, sB, zB, xB, t + 1);
+              load_group(bB, sB, zB, xB, tn, 1);
+            }
+          }
+          reduce_store(tile);
+          bi = bn;
+          tile = tn;
+        } else {
+          if constexpr (ONE) {
+            compute(bA, sA, zA, xA, 0);
+          } else {
+            const int t = body();
+            if (t + 2 < ng) {
+              compute(bA, sA, zA, xA, t);
+              load_group(bA, sA, zA, xA, tile, t + 2);
+              compute(bB, sB, zB, xB, t + 1);
+              compute(bA, sA, zA, xA, t + 2);
+            } else {
+              compute(bA, sA, zA, xA, t);
+              compute(bB, sB, zB, xB, t + 1);
+            }
+          }
+          reduce_store(tile);
+          break;
+        }
+      }
+    };
+    if (ng == 1) tile_loop(std::true_type{});
+    else tile_loop(std::false_type{});
   }
 }
 
@@ -348,36 +433,38 @@ template <int ACT, int FMT>
 hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s);
 
 
-template <int ACT, int MT, int SW, int GPC, int FMT, bool XL>
+template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, bool PT>
 hipError_t decode_launch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
-  constexpr int LB = decode_block_threads(MT, GPC, XL);
-  hipLaunchKernelGGL((decode_kernel<ACT, MT, SW, GPC, FMT, XL, LB>), dim3(c.tiles), dim3(64 * c.W),
+  constexpr int LB = PT ? decode_persistent_threads : decode_block_threads(MT, GPC, XL);
+  hipLaunchKernelGGL((decode_kernel<ACT, MT, SW, GPC, FMT, XL, LB, PT>), dim3(c.grid), dim3(64 * c.W),
                      c.lds_bytes, s, p);
   return hipGetLastError();
 }
 
 // The instantiated set (all free of register spills on gfx950): tiles of two strips with x
 // in LDS, one 16-row tile and one scale group per k-block; every other case one strip.
-template <int ACT, int FMT, int MT, bool XL>
+template <int ACT, int FMT, int MT, bool XL, bool PT>
 hipError_t decode_dispatch_gpc(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
   if constexpr (MT == 1 && XL) {
     if (c.SW == 2) {
-      if (p.GPC == 1) return decode_launch<ACT, 1, 2, 1, FMT, true>(p, c, s);
+      if (p.GPC == 1) return decode_launch<ACT, 1, 2, 1, FMT, true, PT>(p, c, s);
       return hipErrorNotSupported;
     }
   }
   if (c.SW != 1) return hipErrorNotSupported;
   switch (p.GPC) {
-    case 1: return decode_launch<ACT, MT, 1, 1, FMT, XL>(p, c, s);
-    case 2: return decode_launch<ACT, MT, 1, 2, FMT, XL>(p, c, s);
-    default: return decode_launch<ACT, MT, 1, 4, FMT, XL>(p, c, s);
+    case 1: return decode_launch<ACT, MT, 1, 1, FMT, XL, PT>(p, c, s);
+    case 2: return decode_launch<ACT, MT, 1, 2, FMT, XL, PT>(p, c, s);
+    default: return decode_launch<ACT, MT, 1, 4, FMT, XL, PT>(p, c, s);
   }
 }
 
 template <int ACT, int FMT>
 hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
-  if (c.MT == 1) return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 1, true>(p, c, s)
-                                   : decode_dispatch_gpc<ACT, FMT, 1, false>(p, c, s);
+  if (c.MT == 1 && c.persist) return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 1, true, true>(p, c, s)
+                                                 : hipErrorNotSupported;  // x in LDS only
+  if (c.MT == 1) return c.x_in_lds ? decode_dispatch_gpc<ACT, FMT, 1, true, false>(p, c, s)
+                                   : decode_dispatch_gpc<ACT, FMT, 1, false, false>(p, c, s);
   return hipErrorNotSupported;  // launches take at most 16 rows
 }
 

@@ -30,7 +30,9 @@ struct DecodeConfig {
   int KC, NT;        // k-blocks per strip, 16-column strips
   int rows, MT;      // rows of x, 16-row MFMA tiles
   int SW;            // strips per workgroup tile (1, 2 or 4)
-  int tiles;         // workgroups
+  int tiles;         // tiles of SW strips
+  int grid;          // workgroups (persistent: fewer than tiles, each looping over tiles)
+  bool persist;      // persistent workgroups, x staged once for all their tiles
   int W;             // waves per workgroup; wave w streams k-blocks [w*slice, (w+1)*slice)
   int slice;
   int xstride;       // LDS row stride of x (halves)
