@@ -18,6 +18,7 @@ Modules
   packing   eight 4-bit codes per int32 along K; zero-points eight per int32 along N
   dequant   codes + scales (+ zeros | codebook) -> 16-bit weight matrix
   gemm      dequantize-then-matmul reference (fp64) and a brute-force loop version
+  glu       SwiGLU epilogue of a fused gate+up projection, and its parity bound
   storage   bytes and bits per weight of the packed format
   roofline  memory/compute floors and the batch crossover
 
@@ -32,6 +33,7 @@ from .nf4 import nf4_codebook, inverse_normal_cdf
 from .packing import pack_codes, unpack_codes, pack_zeros, unpack_zeros
 from .dequant import dequant_affine, dequant_sym, dequant_nf4
 from .gemm import gemm_ref, gemm_ref_columns, gemm_bruteforce
+from .glu import silu, swiglu_split, swiglu_ref, swiglu_bound
 from .storage import storage_bytes, bits_per_weight, bytes_per_weight
 from . import roofline
 
@@ -43,5 +45,6 @@ __all__ = [
     "pack_codes", "unpack_codes", "pack_zeros", "unpack_zeros",
     "dequant_affine", "dequant_sym", "dequant_nf4",
     "gemm_ref", "gemm_ref_columns", "gemm_bruteforce",
+    "silu", "swiglu_split", "swiglu_ref", "swiglu_bound",
     "storage_bytes", "bits_per_weight", "bytes_per_weight", "roofline",
 ]

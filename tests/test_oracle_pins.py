@@ -306,6 +306,60 @@ def test_gemm_operand_orientation():
     assert y.shape == (2, 16)
 
 
+# ---------------------------------------------------------------- SwiGLU epilogue
+
+
+def test_silu_closed_forms():
+    # sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4, so SiLU(ln 3) = 0.75 ln 3 and
+    # SiLU(-ln 3) = -0.25 ln 3; SiLU(0) = 0; SiLU(a) -> a for large a, -> 0 for very negative a
+    l3 = np.log(3.0)
+    assert abs(oracle.silu(l3) - 0.75 * l3) < 1e-15
+    assert abs(oracle.silu(-l3) + 0.25 * l3) < 1e-15
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-15
+    assert abs(oracle.silu(-40.0)) < 1e-15
+    assert oracle.silu(-1000.0) == 0.0 and np.isfinite(oracle.silu(-1000.0))
+
+
+def test_silu_odd_part_identity():
+    # a*sigmoid(a) - (-a)*sigmoid(-a) = a (sigmoid(a) + sigmoid(-a)) = a, for any a
+    a = np.random.default_rng(5).normal(0, 4, 200)
+    np.testing.assert_allclose(oracle.silu(a) - oracle.silu(-a), a, rtol=0, atol=1e-12)
+
+
+def test_swiglu_gate_columns_come_first():
+    # one-hot x picks row k of W_hat: gate column = ln 3, up column = 2 -> h = 1.5 ln 3;
+    # with the halves swapped it would be SiLU(2) ln 3 = 1.7616 ln 3
+    w = np.zeros((4, 4), np.float16)
+    w[2, 0], w[2, 2] = np.float16(np.log(3.0)), np.float16(2.0)
+    w[1, 1], w[1, 3] = np.float16(0.0), np.float16(5.0)
+    x = np.zeros((2, 4), np.float16)
+    x[0, 2] = 1
+    x[1, 1] = 1
+    h = oracle.swiglu_ref(x, w)
+    g3 = float(np.float16(np.log(3.0)))
+    assert h.shape == (2, 2)
+    assert abs(h[0, 0] - 2.0 * g3 / (1.0 + 1.0 / np.exp(g3))) < 1e-15   # 1.5 ln 3 up to fp16(ln 3)
+    assert abs(h[0, 0] - 1.5 * np.log(3.0)) < 2e-3
+    assert h[1, 1] == 0.0                                                 # gate 0 -> h = 0, up 5
+    assert h[0, 1] == 0.0 and h[1, 0] == 0.0
+
+
+def test_swiglu_bound_covers_first_order_perturbation():
+    # perturbing g and u by up to eps*Y moves h by at most the stated bound
+    rng = np.random.default_rng(6)
+    y = rng.normal(0, 3, (4, 32))
+    eps = 1e-3
+    Y = np.abs(y).max()
+    bound = oracle.swiglu_bound(y, eps)
+    g, u = oracle.swiglu_split(y)
+    for _ in range(20):
+        dg = rng.uniform(-1, 1, g.shape) * eps * Y
+        du = rng.uniform(-1, 1, u.shape) * eps * Y
+        dh = oracle.silu(g + dg) * (u + du) - oracle.silu(g) * u
+        assert np.abs(dh).max() <= bound
+
+
 # ---------------------------------------------------------------- NF4
 
 def test_inverse_normal_matches_library():
