@@ -295,6 +295,72 @@ def sweep(args, torch, w4) -> int:
     return 0
 
 
+def mlp(args, torch, w4) -> int:
+    """The Llama-3-8B-shaped decode MLP per layer (32 layers of distinct weights, asymmetric
+    g128, fp16), replayed from a HIP graph: the fused path is w4a16_gemm_swiglu on the
+    (4096, 28672) gate+up weight then the (14336, 4096) down GEMM; the unfused path runs the
+    plain gate+up GEMM, SiLU(gate) * up as torch elementwise kernels, then the same down GEMM.
+    One JSON line per M with both times per layer."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261204)
+    K, N2, Nd = 4096, 28672, 4096
+    g = 128
+    layers = []
+    for _ in range(32):
+        def weight(k, n):
+            qw = torch.randint(-2**31, 2**31 - 1, (k // 8, n), dtype=torch.int32, device=dev,
+                               generator=gen)
+            packed = w4.pack(qw)
+            sc = (torch.rand((k // g, n), device=dev, generator=gen) * 0.005 + 0.004).half()
+            qz = torch.randint(-2**31, 2**31 - 1, (k // g, n // 8), dtype=torch.int32, device=dev,
+                               generator=gen)
+            return packed, sc, qz
+        layers.append((weight(K, N2), weight(N2 // 2, Nd)))
+    for M in (1, 4, 16, 64, 256):
+        x = torch.randn((M, K), device=dev, generator=gen).half()
+        h = torch.empty((M, N2 // 2), device=dev, dtype=torch.float16)
+        y2 = torch.empty((M, N2), device=dev, dtype=torch.float16)
+        y = torch.empty((M, Nd), device=dev, dtype=torch.float16)
+        ws = torch.empty(max(w4.workspace_bytes(M, K, N2, g), w4.workspace_bytes(M, N2 // 2, Nd, g), 256),
+                         dtype=torch.uint8, device=dev)
+
+        def fused():
+            for (gu, dn) in layers:
+                w4.gemm_swiglu(x, *gu, g, out=h, workspace=ws)
+                w4.gemm(h, *dn, g, out=y, workspace=ws)
+
+        def unfused():
+            for (gu, dn) in layers:
+                w4.gemm(x, *gu, g, out=y2, workspace=ws)
+                hh = torch.nn.functional.silu(y2[:, :N2 // 2]) * y2[:, N2 // 2:]
+                w4.gemm(hh, *dn, g, out=y, workspace=ws)
+
+        res = {}
+        for name, fn in (("fused_us", fused), ("unfused_us", unfused)):
+            fn()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = round(e0.elapsed_time(e1) * 1e3 / (args.steps * len(layers)), 2)
+            del graph
+        res["speedup"] = round(res["unfused_us"] / res["fused_us"], 3)
+        print(json.dumps({"config": "mlp llama3-8b (gate+up 4096x28672 with SwiGLU, down 14336x4096)",
+                          "M": M, "swiglu_kernel": w4.kernel_name(M, K, N2, g), **res}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +370,8 @@ def main() -> int:
     ap.add_argument("--m", type=int, default=None, help="rows of x (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a HIP graph")
+    ap.add_argument("--mlp", action="store_true",
+                    help="time the fused SwiGLU decode MLP against the unfused path, per layer")
     ap.add_argument("--sweep", action="store_true",
                     help="per-(config, shape, M) timing table of every benchmark config, one JSON "
                          "line per row, instead of the step benchmark")
@@ -332,6 +400,8 @@ def main() -> int:
     import weight_only_int4_w4a16_amd as w4
     from weight_only_int4_w4a16_amd import synth
 
+    if args.mlp:
+        return mlp(args, torch, w4)
     if args.sweep:
         return sweep(args, torch, w4)
 

@@ -104,6 +104,29 @@ w4a16_status w4a16_gemm_nf4(const void* x, int M, int K, int N, w4a16_dtype act,
                             w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* The fused gate+up projection of a gated MLP with its SwiGLU epilogue: the kernels form
+ * g = x W_gate and u = x W_up in fp32 and store only h = SiLU(g) * u = g / (1 + exp(-g)) * u
+ * (the pages' next step after the linear layer, "4.3 Weight-only INT4", closing section:
+ * operator fusion; the MLP is the Llama one whose shapes the pages' decode examples use).
+ *   packed, scales, qzeros  the (K, N2) weight holding W_gate in columns [0, N2/2) and W_up
+ *                   in [N2/2, N2), packed and laid out exactly as for w4a16_gemm
+ *   out       [out] out_dtype [M][N2/2]
+ *   workspace       >= w4a16_workspace_bytes(M, K, N2, group_size) bytes (as for w4a16_gemm)
+ * N2 must be a multiple of 32 (W4A16_ERR_UNSUPPORTED otherwise). Other arguments, errors and
+ * determinism as for w4a16_gemm; one launch per call for M <= 16 (two with a K split). */
+w4a16_status w4a16_gemm_swiglu(const void* x, int M, int K, int N2, w4a16_dtype act,
+                               const int32_t* packed, const void* scales, const int32_t* qzeros,
+                               int group_size, void* out, w4a16_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* NF4 counterpart of w4a16_gemm_swiglu (absmax [K/block_size][N2] fp16, codebook as for
+ * w4a16_gemm_nf4). */
+w4a16_status w4a16_gemm_nf4_swiglu(const void* x, int M, int K, int N2, w4a16_dtype act,
+                                   const int32_t* packed, const uint16_t* absmax,
+                                   const uint16_t* codebook, int block_size, void* out,
+                                   w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Test hook: write W_hat[K][N] (row-major, in `wdtype` = F16 or BF16) using the same
  * device dequantization routine the GEMM kernels use where they form W_hat (the batched
  * kernel, and the decode kernel for bf16 activations and NF4). The fp16 affine decode

@@ -97,6 +97,18 @@ def run_gemm(case, d, out_dtype=None):
     return y
 
 
+def run_swiglu(case, d, out_dtype=None):
+    import weight_only_int4_w4a16_amd as w4
+    if case["nf4"]:
+        h = w4.gemm_nf4_swiglu(d["x"], d["packed"], d["scales"], d["codebook"], case["g"],
+                               out_dtype=out_dtype)
+    else:
+        h = w4.gemm_swiglu(d["x"], d["packed"], d["scales"], d["qzeros"], case["g"],
+                           out_dtype=out_dtype)
+    torch_mod().cuda.synchronize()
+    return h
+
+
 def assert_close(y: np.ndarray, y_ref: np.ndarray, what: str = ""):
     err = np.max(np.abs(y - y_ref)) if y.size else 0.0
     bound = RTOL * np.max(np.abs(y_ref)) if y.size else 0.0

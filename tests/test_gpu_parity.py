@@ -14,7 +14,7 @@ import pytest
 import oracle
 from weight_only_int4_w4a16_amd import synth
 
-from gpu_common import (assert_close, device_inputs, from_dev, oracle_columns, out_values,
+from gpu_common import (assert_close, device_inputs, from_dev, oracle_columns, out_values, run_swiglu,
                         require_gpu, rtn_case, run_gemm, sample_strips, to_dev, torch_mod)
 
 pytestmark = pytest.mark.gpu
@@ -135,6 +135,74 @@ def test_gemm_small_all_outputs(M, K, N, g, act, fmt):
         # bf16 output is the nearest-even rounding of the same fp32 accumulation
         exp = oracle.round_nearest_bf16_bits(from_dev(y32).astype(np.float64))
         assert np.array_equal(from_dev(y16), exp)
+
+
+# SwiGLU epilogue on a fused gate+up weight [K, N2]: decode (x in LDS and not, persistent
+# workgroups, one and several groups per wave) and batched (both tiles, with and without a
+# K split), every format
+SWIGLU = [
+    (1, 512, 64, 128, "f16", "asym"),
+    (3, 352, 96, 32, "bf16", "asym"),
+    (16, 1024, 128, 64, "f16", "sym"),
+    (5, 14336, 64, 64, "f16", "asym"),       # x from global (too large for LDS at 5 rows)
+    (12, 4096, 16416, 128, "f16", "asym"),   # persistent, one group per wave
+    (9, 4224, 16448, 64, "bf16", "nf4"),     # persistent, several groups per wave
+    (2, 1024, 96, 64, "bf16", "nf4"),
+    (17, 512, 64, 128, "bf16", "asym"),      # batched 64x256, K split
+    (130, 2144, 96, 32, "f16", "sym"),
+    (300, 1024, 544, 128, "f16", "asym"),    # batched 64x256, ragged tile
+    (257, 2080, 2080, 32, "f16", "nf4"),
+    (513, 2080, 16416, 32, "bf16", "asym"),  # batched 128x512
+]
+
+
+@pytest.mark.parametrize("M,K,N2,g,act,fmt", SWIGLU)
+def test_swiglu_all_outputs(M, K, N2, g, act, fmt):
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    _announce(f"swiglu M={M} K={K} N2={N2} g={g} {act} {fmt} kernel={w4.kernel_name(M, K, N2, g)}")
+    c = rtn_case(M, K, N2, g, act, sym=(fmt == "sym"), seed=11 * M + K, nf4=(fmt == "nf4"))
+    d = device_inputs(c)
+    y_ref = oracle.gemm_ref(c["x"], c["w_hat"], act)
+    h_ref = oracle.swiglu_ref(c["x"], c["w_hat"], act)
+    bound = oracle.swiglu_bound(y_ref)
+    h32 = from_dev(run_swiglu(c, d, out_dtype=torch.float32)).astype(np.float64)
+    assert h32.shape == (M, N2 // 2)
+    assert np.all(np.isfinite(h32))
+    err = np.max(np.abs(h32 - h_ref))
+    assert err <= bound, f"fp32 out: max|h - h_ref| = {err:.3e} > {bound:.3e}"
+    # 16-bit output: the same fp32 value rounded once to the activation type
+    h16 = from_dev(run_swiglu(c, d))
+    if act == "f16":
+        assert np.array_equal(h16.view(np.uint16), h32.astype(np.float32).astype(np.float16).view(np.uint16))
+    else:
+        assert np.array_equal(h16, oracle.round_nearest_bf16_bits(h32))
+
+
+def test_swiglu_gate_and_up_halves():
+    """One-hot rows: h is SiLU of the gate half's dequantized row times the up half's."""
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    for M in (4, 40):   # decode and batched
+        c = rtn_case(M, 256, 64, 64, "f16", seed=21 + M)
+        x = np.zeros((M, 256), np.float16)
+        for m in range(M):
+            x[m, (37 * m) % 256] = 1
+        c["x"] = x
+        d = device_inputs(c)
+        h = from_dev(run_swiglu(c, d, out_dtype=torch.float32)).astype(np.float64)
+        rows = c["w_hat"].astype(np.float64)[[(37 * m) % 256 for m in range(M)]]
+        h_ref = oracle.silu(rows[:, :32]) * rows[:, 32:]
+        assert np.max(np.abs(h - h_ref)) <= 1e-6 * max(1.0, np.max(np.abs(h_ref)))
+
+
+def test_swiglu_rejects_odd_strip_halves():
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    c = rtn_case(2, 256, 48, 64, "f16", seed=5)   # N2 = 48: halves of 24 columns
+    d = device_inputs(c)
+    with pytest.raises(w4.W4A16Error):
+        run_swiglu(c, d)
 
 
 def test_gemm_m0_is_noop():

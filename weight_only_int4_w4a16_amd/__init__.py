@@ -7,7 +7,9 @@ fp32 accumulation. The compute runs in hand-written HIP kernels behind the C ABI
 does not load the library; the first call does, and raises if it was not built.
 """
 from .binding import (W4A16Error, F16, BF16, F32, lib, packed_bytes, workspace_bytes, pack,
-                      gemm, gemm_nf4, dequant, dequant_nf4, kernel_name, version)
+                      gemm, gemm_nf4, gemm_swiglu, gemm_nf4_swiglu, dequant, dequant_nf4,
+                      kernel_name, version)
 
 __all__ = ["W4A16Error", "F16", "BF16", "F32", "lib", "packed_bytes", "workspace_bytes", "pack", "gemm",
-           "gemm_nf4", "dequant", "dequant_nf4", "kernel_name", "version"]
+           "gemm_nf4", "gemm_swiglu", "gemm_nf4_swiglu", "dequant", "dequant_nf4", "kernel_name",
+           "version"]

@@ -46,6 +46,10 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemm.restype = i32
     L.w4a16_gemm_nf4.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
     L.w4a16_gemm_nf4.restype = i32
+    L.w4a16_gemm_swiglu.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
+    L.w4a16_gemm_swiglu.restype = i32
+    L.w4a16_gemm_nf4_swiglu.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
+    L.w4a16_gemm_nf4_swiglu.restype = i32
     L.w4a16_dequant.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
     L.w4a16_dequant.restype = i32
     L.w4a16_dequant_nf4.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
@@ -176,6 +180,46 @@ def gemm_nf4(x, packed, absmax, codebook, block_size: int = 64, out_dtype=None, 
                               _ptr(codebook), block_size, _ptr(out), _dt(out.dtype), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size(), _stream(x))
     _check(st, "w4a16_gemm_nf4")
+    return out
+
+
+def gemm_swiglu(x, packed, scales, qzeros, group_size: int, out_dtype=None, out=None,
+                workspace=None):
+    """``h = SiLU(x @ W_gate) * (x @ W_up)`` for a fused gate+up weight ``[K, N2]`` (gate
+    columns first; ``scales[K/g, N2]``, ``qzeros[K/g, N2/8]`` or None); ``h[M, N2/2]``."""
+    torch = _torch()
+    M, K = x.shape
+    N2 = scales.shape[1]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N2 // 2), dtype=out_dtype, device=x.device)
+    if scales.dtype != x.dtype:
+        raise W4A16Error("scales must have the activation dtype")
+    ws = _workspace(x.device, workspace_bytes(M, K, N2, group_size) if M else 0, workspace)
+    st = lib().w4a16_gemm_swiglu(_ptr(x), M, K, N2, _dt(x.dtype), _ptr(packed), _ptr(scales),
+                                 _ptr(qzeros), group_size, _ptr(out), _dt(out.dtype), _ptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(x))
+    _check(st, "w4a16_gemm_swiglu")
+    return out
+
+
+def gemm_nf4_swiglu(x, packed, absmax, codebook, block_size: int = 64, out_dtype=None, out=None,
+                    workspace=None):
+    """NF4 counterpart of :func:`gemm_swiglu`."""
+    torch = _torch()
+    M, K = x.shape
+    N2 = absmax.shape[1]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N2 // 2), dtype=out_dtype, device=x.device)
+    if absmax.dtype != torch.float16 or codebook.dtype != torch.float16:
+        raise W4A16Error("NF4 absmax and codebook are fp16")
+    ws = _workspace(x.device, workspace_bytes(M, K, N2, block_size) if M else 0, workspace)
+    st = lib().w4a16_gemm_nf4_swiglu(_ptr(x), M, K, N2, _dt(x.dtype), _ptr(packed), _ptr(absmax),
+                                     _ptr(codebook), block_size, _ptr(out), _dt(out.dtype),
+                                     _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(x))
+    _check(st, "w4a16_gemm_nf4_swiglu")
     return out
 
 

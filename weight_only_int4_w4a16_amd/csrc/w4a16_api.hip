@@ -33,7 +33,7 @@ size_t workspace_need(int M, int K, int N, int gs) {
   GemmArgs a{};
   a.M = M; a.K = K; a.N = N; a.group_size = gs;
   if (use_tiled(a)) return w4a16::tiled_workspace_bytes(M, K, N);
-  return w4a16::decode_config(M < 16 ? M : 16, K, N, gs, w4a16::ACT_F16).workspace_bytes;
+  return w4a16::decode_config(M < 16 ? M : 16, K, N, gs, false).workspace_bytes;
 }
 
 w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
@@ -45,6 +45,7 @@ w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
   if (a.M == 0) return W4A16_OK;
   if (!a.x || !a.packed || !a.scales || !a.out) return W4A16_ERR_ARG;
   if (a.nf4 && !a.codebook) return W4A16_ERR_ARG;
+  if (a.glu && a.N % 32) return W4A16_ERR_UNSUPPORTED;  // each half whole 16-column strips
   if (!aligned(a.x, 16) || !aligned(a.packed, 16) || !aligned(a.out, 16)) return W4A16_ERR_ARG;
   if (!aligned(a.scales, 2) || (a.qzeros && !aligned(a.qzeros, 4))) return W4A16_ERR_ARG;
   if (a.codebook && !aligned(a.codebook, 2)) return W4A16_ERR_ARG;
@@ -93,6 +94,41 @@ w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
   a.qzeros = reinterpret_cast<const uint32_t*>(qzeros);
   a.codebook = nullptr; a.nf4 = false;
   a.group_size = group_size;
+  a.out = out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.stream = static_cast<hipStream_t>(stream);
+  return gemm_common(a, act, out_dtype);
+}
+
+w4a16_status w4a16_gemm_swiglu(const void* x, int M, int K, int N2, w4a16_dtype act,
+                               const int32_t* packed, const void* scales, const int32_t* qzeros,
+                               int group_size, void* out, w4a16_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  GemmArgs a{};
+  a.x = x; a.M = M; a.K = K; a.N = N2;
+  a.packed = reinterpret_cast<const uint32_t*>(packed);
+  a.scales = scales;
+  a.qzeros = reinterpret_cast<const uint32_t*>(qzeros);
+  a.codebook = nullptr; a.nf4 = false; a.glu = true;
+  a.group_size = group_size;
+  a.out = out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.stream = static_cast<hipStream_t>(stream);
+  return gemm_common(a, act, out_dtype);
+}
+
+w4a16_status w4a16_gemm_nf4_swiglu(const void* x, int M, int K, int N2, w4a16_dtype act,
+                                   const int32_t* packed, const uint16_t* absmax,
+                                   const uint16_t* codebook, int block_size, void* out,
+                                   w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  GemmArgs a{};
+  a.x = x; a.M = M; a.K = K; a.N = N2;
+  a.packed = reinterpret_cast<const uint32_t*>(packed);
+  a.scales = absmax;
+  a.qzeros = nullptr;
+  a.codebook = codebook; a.nf4 = true; a.glu = true;
+  a.group_size = block_size;
   a.out = out;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   a.stream = static_cast<hipStream_t>(stream);

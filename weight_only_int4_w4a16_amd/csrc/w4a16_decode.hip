@@ -34,6 +34,7 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
   c.tiles = c.NT / SW;
   c.grid = c.tiles;
   c.persist = false;
+  c.glu = false;
   c.slice = ceil_div(c.KC, W);
   c.W = ceil_div(c.KC, c.slice);  // drop waves left without blocks
   c.xstride = c.slice * 128 + 8;
@@ -59,7 +60,7 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
 // loads are in flight while the wave partials are summed), the launch one more. Measured:
 // 4096x28672 at M=16 33.5 -> 23.0 us, 8192x57344 at M=8 77.9 -> 54.7 us, 8192x10240 at M=8
 // 21.0 -> 18.2 us; at M=4 the same rule would lose (4096x28672 17.3 -> 20.4 us).
-DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
+DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu) {
   const int KC = ceil_div(K, 128), NT = N / 16;
   const int rows = M < 16 ? M : 16, MT = ceil_div(rows, 16);
   const int GPC = 128 / group_size;
@@ -68,13 +69,14 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
   const int waves_per_cu = wmax == 16 ? 16 : 8;
   DecodeConfig best{}, pbest{};
   long best_cost = -1, best_rounds = 0, pbest_cost = -1;
-  for (int SW = 2; SW >= 1; SW >>= 1) {
+  for (int SW = 2; SW >= (glu ? 2 : 1); SW >>= 1) {  // SwiGLU tiles: a gate and an up strip
     if (NT % SW) continue;
-    if (SW > 1 && !(x_in_lds && MT == 1 && GPC == 1)) continue;
+    if (SW > 1 && !glu && !(x_in_lds && MT == 1 && GPC == 1)) continue;
     const int D = decode_group_blocks(SW, GPC, x_in_lds);  // k-blocks per pipeline group
     for (int W = wmax; W >= 1; W >>= 1) {
       if (W > 1 && W > KC / D) continue;  // every wave streams at least one whole group
-      const DecodeConfig c = geometry(M, K, N, x_in_lds, SW, W);
+      DecodeConfig c = geometry(M, K, N, x_in_lds, SW, W);
+      c.glu = glu;
       if (c.lds_bytes > kMaxLds) continue;
       int wg_per_cu = waves_per_cu / W;
       const int by_lds = (int)(kMaxLds / c.lds_bytes);
@@ -114,25 +116,26 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds) {
 }  // namespace
 
 // x goes to LDS when it fits beside the reduction area; otherwise it is read per k-block
-DecodeConfig decode_config(int M, int K, int N, int group_size, int act) {
-  (void)act;  // every instantiated configuration exists for both activation types
+// (every instantiated configuration exists for both activation types)
+DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu) {
   const int rows = M < 16 ? M : 16;
   const size_t xbytes = (size_t)rows * ceil_div(K, 128) * 128 * 2;
   if (xbytes <= kXldsBytes) {
-    const DecodeConfig c = choose(M, K, N, group_size, true);
+    const DecodeConfig c = choose(M, K, N, group_size, true, glu);
     if (c.W > 0) return c;
   }
-  return choose(M, K, N, group_size, false);
+  return choose(M, K, N, group_size, false, glu);
 }
 
 // Rows of x one launch takes: at most 16, one MFMA tile (larger M goes to the batched
 // kernel; a caller of this launcher with more rows gets several launches).
-DecodeConfig decode_launch_config(int M, int K, int N, int group_size, int act) {
-  return decode_config(M < 16 ? M : 16, K, N, group_size, act);
+DecodeConfig decode_launch_config(int M, int K, int N, int group_size, bool glu) {
+  return decode_config(M < 16 ? M : 16, K, N, group_size, glu);
 }
 
 const char* decode_name(int M, int K, int N, int group_size, int act) {
-  const DecodeConfig c = decode_launch_config(M, K, N, group_size, act);
+  (void)act;
+  const DecodeConfig c = decode_launch_config(M, K, N, group_size, false);
   if (c.persist) return c.SW == 1 ? "w4a16_decode_sw1_persist" : "w4a16_decode_sw2_persist";
   return c.SW == 1 ? "w4a16_decode_sw1" : "w4a16_decode_sw2";
 }
@@ -140,7 +143,7 @@ const char* decode_name(int M, int K, int N, int group_size, int act) {
 hipError_t launch_decode(const GemmArgs& a) {
   const size_t osz = a.out_dtype == 2 ? 4 : 2;
   for (int r0 = 0; r0 < a.M;) {
-    const DecodeConfig c = decode_launch_config(a.M - r0, a.K, a.N, a.group_size, a.act);
+    const DecodeConfig c = decode_launch_config(a.M - r0, a.K, a.N, a.group_size, a.glu);
     const int rows = c.rows;
     DecodeParams p;
     p.x = static_cast<const uint16_t*>(a.x) + (size_t)r0 * a.K;
@@ -151,7 +154,7 @@ hipError_t launch_decode(const GemmArgs& a) {
     p.scales = static_cast<const uint16_t*>(a.scales);
     p.qzeros = a.qzeros;
     p.codebook = a.codebook;
-    p.out = static_cast<char*>(a.out) + (size_t)r0 * a.N * osz;
+    p.out = static_cast<char*>(a.out) + (size_t)r0 * (a.glu ? a.N / 2 : a.N) * osz;
     p.out_dtype = a.out_dtype;
     p.KC = c.KC;
     p.NG = a.K / a.group_size;
@@ -161,6 +164,7 @@ hipError_t launch_decode(const GemmArgs& a) {
     p.xstride = c.xstride;
     p.xslice = c.xslice;
     p.GPC = 128 / a.group_size;
+    p.half = a.N / 32;
     hipError_t e;
     const int fmt = a.nf4 ? FMT_NF4 : a.qzeros ? FMT_ASYM : FMT_SYM;
     if (a.act == ACT_F16) {

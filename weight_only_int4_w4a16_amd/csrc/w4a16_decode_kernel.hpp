@@ -59,6 +59,7 @@ struct DecodeParams {
   int xstride;   // LDS row stride of x in halves (XL)
   int xslice;    // LDS halves reserved per wave for its slice of x (XL)
   int GPC;       // scale groups per 128-k block (128 / group size)
+  int half;      // GLU: strips per half of the fused gate+up weight (N / 32)
 };
 
 constexpr int kXRegs = 2;  // 16-byte chunks of x per lane staged in registers ahead of the weights
@@ -75,10 +76,11 @@ constexpr int decode_block_threads(int MT, int GPC, bool XL) {
 constexpr int decode_persistent_threads = 512;
 
 // k-blocks per pipeline group: four blocks (4 KiB) per group with x in LDS, halved for four
-// scale groups per block (their scales and zero words would not fit the 128 registers of a
-// 1024-thread workgroup); one block when the activation fragments travel with the codes.
+// scale groups per block, and for two with two strips per tile (their scales and zero words
+// would not fit the 128 registers of a 1024-thread workgroup); one block when the
+// activation fragments travel with the codes.
 constexpr int decode_group_blocks(int SW, int GPC, bool XL) {
-  return XL ? (GPC == 4 ? 2 : 4) / SW : 1;
+  return XL ? (GPC == 4 || (GPC == 2 && SW == 2) ? 2 : 4) / SW : 1;
 }
 
 // fp16 affine formats multiply integer-valued operands and
@@ -94,9 +96,12 @@ __device__ __forceinline__ int tile_of(int b, int G) {
 
 // PT (persistent tiles): the grid is smaller than the tile count and each workgroup loops
 // over tiles blockIdx.x, + gridDim.x, ... with x staged once.
-template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, int LB, bool PT>
+// GLU: the weight is a fused gate+up projection [K][2 Nh] (gate columns first); tile t pairs
+// gate strip t with up strip t + Nh/16 and stores h = SiLU(gate) * up, [M][Nh].
+template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, int LB, bool PT, bool GLU>
 __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   typedef typename ActT<ACT>::type AT;
+  static_assert(!GLU || SW == 2, "a SwiGLU tile is one gate strip and one up strip");
   constexpr int D = decode_group_blocks(SW, GPC, XL);  // k-blocks per group
   constexpr int SPG = 4 / GPC;        // 32-k steps per scale group
   constexpr bool ZEROS = FMT == FMT_ASYM;
@@ -110,6 +115,10 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   const int kc1 = min(kc0 + p.slice, KC);
   const int ng = (kc1 - kc0 + D - 1) / D;  // groups of this wave
   const int shift = 4 * (lane & 7);  // nibble of the lane's column in its zero word
+  // strip sw of a tile: SW adjacent strips, or (GLU) the gate strip and its up strip
+  auto strip_of = [&](int tile, int sw) __attribute__((always_inline)) {
+    return GLU ? tile + sw * p.half : tile * SW + sw;
+  };
 
   float* red = reinterpret_cast<float*>(lds);                                   // [W][SW][rows][16]
   uint16_t* xs = reinterpret_cast<uint16_t*>(red + (size_t)p.W * SW * rows * 16) +
@@ -123,19 +132,19 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
 
   auto load_group = [&](u4_t(&b)[D][SW], uint16_t(&s)[D][SW][GPC], uint32_t(&z)[D][SW][GPC],
                         u4_t(&xf)[XL ? 1 : MT][4], int tile, int t) __attribute__((always_inline)) {
-    const int col = tile * SW * 16 + (lane & 15);  // this lane's column in strip 0 of the tile
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int kc = min(kc0 + t * D + d, kc1 - 1);  // past the slice: reload its last block
 #pragma unroll
       for (int sw = 0; sw < SW; ++sw) {
-        const int nt = tile * SW + sw;
+        const int nt = strip_of(tile, sw);
+        const int col = nt * 16 + (lane & 15);  // this lane's column
         b[d][sw] = __builtin_nontemporal_load(p.packed + ((size_t)nt * KC + kc) * 64 + lane);
 #pragma unroll
         for (int gi = 0; gi < GPC; ++gi) {
           const int g = min(kc * GPC + gi, p.NG - 1);  // groups past K are never used
-          s[d][sw][gi] = p.scales[(size_t)g * N + col + sw * 16];
-          if constexpr (ZEROS) z[d][sw][gi] = p.qzeros[(size_t)g * (N >> 3) + ((col + sw * 16) >> 3)];
+          s[d][sw][gi] = p.scales[(size_t)g * N + col];
+          if constexpr (ZEROS) z[d][sw][gi] = p.qzeros[(size_t)g * (N >> 3) + (col >> 3)];
         }
       }
       if constexpr (!XL) {
@@ -308,13 +317,27 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
         }
     __syncthreads();
     const int per_wave = SW * rows * 16;
-    for (int e = threadIdx.x; e < per_wave; e += blockDim.x) {
-      float v = 0.f;
-      for (int w = 0; w < p.W; ++w) v += red[(size_t)w * per_wave + e];
-      const int sw = e / (rows * 16);
-      const int rem = e - sw * rows * 16;
-      const int m = rem >> 4, c = rem & 15;
-      store_out(p.out, (size_t)m * N + (size_t)(tile * SW + sw) * 16 + c, v, p.out_dtype);
+    if constexpr (GLU) {
+      // h = SiLU(g) * u = g / (1 + exp(-g)) * u, into the [M][N/2] output
+      for (int e = threadIdx.x; e < rows * 16; e += blockDim.x) {
+        float g = 0.f, u = 0.f;
+        for (int w = 0; w < p.W; ++w) {
+          g += red[(size_t)w * per_wave + e];
+          u += red[(size_t)w * per_wave + rows * 16 + e];
+        }
+        const int m = e >> 4, c = e & 15;
+        store_out(p.out, (size_t)m * (N >> 1) + (size_t)tile * 16 + c, g / (1.0f + __expf(-g)) * u,
+                  p.out_dtype);
+      }
+    } else {
+      for (int e = threadIdx.x; e < per_wave; e += blockDim.x) {
+        float v = 0.f;
+        for (int w = 0; w < p.W; ++w) v += red[(size_t)w * per_wave + e];
+        const int sw = e / (rows * 16);
+        const int rem = e - sw * rows * 16;
+        const int m = rem >> 4, c = rem & 15;
+        store_out(p.out, (size_t)m * N + (size_t)(tile * SW + sw) * 16 + c, v, p.out_dtype);
+      }
     }
     if constexpr (PT) __syncthreads();  // the next tile's partials overwrite red
   };
@@ -433,11 +456,11 @@ template <int ACT, int FMT>
 hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s);
 
 
-template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, bool PT>
+template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, bool PT, bool GLU>
 hipError_t decode_launch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
   constexpr int LB = PT ? decode_persistent_threads : decode_block_threads(MT, GPC, XL);
-  hipLaunchKernelGGL((decode_kernel<ACT, MT, SW, GPC, FMT, XL, LB, PT>), dim3(c.grid), dim3(64 * c.W),
-                     c.lds_bytes, s, p);
+  hipLaunchKernelGGL((decode_kernel<ACT, MT, SW, GPC, FMT, XL, LB, PT, GLU>), dim3(c.grid),
+                     dim3(64 * c.W), c.lds_bytes, s, p);
   return hipGetLastError();
 }
 
@@ -445,17 +468,25 @@ hipError_t decode_launch(const DecodeParams& p, const DecodeConfig& c, hipStream
 // in LDS, one 16-row tile and one scale group per k-block; every other case one strip.
 template <int ACT, int FMT, int MT, bool XL, bool PT>
 hipError_t decode_dispatch_gpc(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
+  if (c.glu) {  // gate/up strip pairs, every group size
+    if (c.SW != 2) return hipErrorNotSupported;
+    switch (p.GPC) {
+      case 1: return decode_launch<ACT, MT, 2, 1, FMT, XL, PT, true>(p, c, s);
+      case 2: return decode_launch<ACT, MT, 2, 2, FMT, XL, PT, true>(p, c, s);
+      default: return decode_launch<ACT, MT, 2, 4, FMT, XL, PT, true>(p, c, s);
+    }
+  }
   if constexpr (MT == 1 && XL) {
     if (c.SW == 2) {
-      if (p.GPC == 1) return decode_launch<ACT, 1, 2, 1, FMT, true, PT>(p, c, s);
+      if (p.GPC == 1) return decode_launch<ACT, 1, 2, 1, FMT, true, PT, false>(p, c, s);
       return hipErrorNotSupported;
     }
   }
   if (c.SW != 1) return hipErrorNotSupported;
   switch (p.GPC) {
-    case 1: return decode_launch<ACT, MT, 1, 1, FMT, XL, PT>(p, c, s);
-    case 2: return decode_launch<ACT, MT, 1, 2, FMT, XL, PT>(p, c, s);
-    default: return decode_launch<ACT, MT, 1, 4, FMT, XL, PT>(p, c, s);
+    case 1: return decode_launch<ACT, MT, 1, 1, FMT, XL, PT, false>(p, c, s);
+    case 2: return decode_launch<ACT, MT, 1, 2, FMT, XL, PT, false>(p, c, s);
+    default: return decode_launch<ACT, MT, 1, 4, FMT, XL, PT, false>(p, c, s);
   }
 }
 

@@ -20,6 +20,7 @@ struct GemmArgs {
   int group_size;
   void* out;
   int out_dtype;           // 0 fp16, 1 bf16, 2 fp32
+  bool glu;                // N columns = gate | up halves; out = SiLU(gate) * up, [M][N/2]
   void* workspace;         // scratch for split-K partial tiles (no state between calls)
   size_t workspace_bytes;
   hipStream_t stream;
@@ -33,6 +34,7 @@ struct DecodeConfig {
   int tiles;         // tiles of SW strips
   int grid;          // workgroups (persistent: fewer than tiles, each looping over tiles)
   bool persist;      // persistent workgroups, x staged once for all their tiles
+  bool glu;          // SwiGLU: tiles pair a gate strip with its up strip
   int W;             // waves per workgroup; wave w streams k-blocks [w*slice, (w+1)*slice)
   int slice;
   int xstride;       // LDS row stride of x (halves)
@@ -41,7 +43,7 @@ struct DecodeConfig {
   size_t lds_bytes;  // dynamic LDS per workgroup
   size_t workspace_bytes;
 };
-DecodeConfig decode_config(int M, int K, int N, int group_size, int act);
+DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu);
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

@@ -71,7 +71,8 @@ struct TiledParams {
   int KC, NT, NG;      // k-blocks, strips, scale groups along K
   int tiles_m, tiles_n;
   int S, kps;          // K slices and k-blocks per slice
-  float* partials;     // [S][tiles_m * 128][N] fp32 (S > 1)
+  float* partials;     // [S][tiles_m * tile rows][N] fp32 (S > 1)
+  int half;            // GLU: strips per half of the fused gate+up weight (NT / 2)
 };
 
 // workgroup -> output tile, so that tiles sharing weight columns run on the same XCD
@@ -80,7 +81,11 @@ __device__ __forceinline__ int tile_of(int b, int G) {
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
-template <int ACT, int GPC, int FMT, class T>
+// GLU: the weight is a fused gate+up projection [K][2 Nh] (gate columns first). A wave's
+// first strip pair is two gate strips, its second the matching up strips, and the output is
+// h = SiLU(gate) * up, [M][Nh] (with K split, both halves go to the partials and the GLU
+// reduce kernel forms h).
+template <int ACT, int GPC, int FMT, class T, bool GLU>
 __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   constexpr int kMT = T::kMT, kBM = T::kBM, kWaves = T::kWaves, kThreads = T::kThreads;
   constexpr int kAChunks = T::kAChunks;
@@ -100,6 +105,11 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   const int kc0 = z * p.kps;
   const int kc1 = min(kc0 + p.kps, KC);
   const int nt0 = tn * (kWaves * kStrips) + wave * kStrips;  // this wave's first strip
+  const int g0 = tn * (kWaves * 2) + wave * 2;                // GLU: its first gate strip
+  // strip of pair pr, half h (h = lane/16 % 2), clamped in bounds for loads
+  auto strip_of = [&](int pr, int h) {
+    return GLU ? min(g0 + h, p.half - 1) + pr * p.half : min(nt0 + 2 * pr + h, p.NT - 1);
+  };
   const int shift = 4 * (lane & 7);
 
   // ---- one k-block of operands: the activation tile slice this thread copies to LDS, and
@@ -125,7 +135,7 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
 #pragma unroll
     for (int pr = 0; pr < kPairs; ++pr) {
       // strips past N: loaded in bounds, never stored
-      const int nt = min(nt0 + 2 * pr + ((lane >> 4) & 1), p.NT - 1);
+      const int nt = strip_of(pr, (lane >> 4) & 1);
       const int col = nt * 16 + (lane & 15);
       const u4_t* blk = p.packed + ((size_t)nt * KC + kc) * 64;
       const int c0 = 16 * (lane >> 5) + (lane & 15);
@@ -223,6 +233,27 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   // ---- epilogue ----
   // lane l holds column 32*pair + l%32 and rows 32*mt + 8*(i/4) + 4*(l/32) + i%4, i < 16
   const size_t slice_stride = (size_t)p.tiles_m * kBM * N;
+  if constexpr (GLU) {
+    const int gs = g0 + ((lane >> 4) & 1);  // gate strip of this lane's columns
+    if (gs < p.half) {
+      const int col = gs * 16 + (lane & 15);  // column in the gate half and in h
+      const int nh = N >> 1;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + mt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          const float g = acc[mt][0][i], u = acc[mt][1][i];
+          if (p.S == 1) {
+            if (m < M) store_out(p.out, (size_t)m * nh + col, g / (1.0f + __expf(-g)) * u, p.out_dtype);
+          } else if (m < M) {
+            p.partials[z * slice_stride + (size_t)m * N + col] = g;
+            p.partials[z * slice_stride + (size_t)m * N + nh + col] = u;
+          }
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int pr = 0; pr < kPairs; ++pr) {
     const int nt = nt0 + 2 * pr + ((lane >> 4) & 1);
@@ -256,6 +287,26 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   for (int zz = 1; zz < S; ++zz) v += *reinterpret_cast<const f4_t*>(partials + zz * slice_stride + e);
 #pragma unroll
   for (int c = 0; c < 4; ++c) store_out(out, e + c, v[c], out_dtype);
+}
+
+// h[m, n] = SiLU(g) * u with g, u the slice sums (in slice order) of partial[s][m][n] and
+// partial[s][m][n + Nh], n < Nh; four consecutive columns per thread (Nh is a multiple of 16)
+__global__ __launch_bounds__(256) void splitk_reduce_glu_kernel(const float* __restrict__ partials, int M,
+                                                                int Nh, int S, size_t slice_stride,
+                                                                void* out, int out_dtype) {
+  const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t e = i4 * 4;
+  if (e >= (size_t)M * Nh) return;
+  const size_t m = e / Nh, n = e - m * Nh;
+  const size_t pg = m * 2 * Nh + n;
+  f4_t g = *reinterpret_cast<const f4_t*>(partials + pg);
+  f4_t u = *reinterpret_cast<const f4_t*>(partials + pg + Nh);
+  for (int zz = 1; zz < S; ++zz) {
+    g += *reinterpret_cast<const f4_t*>(partials + zz * slice_stride + pg);
+    u += *reinterpret_cast<const f4_t*>(partials + zz * slice_stride + pg + Nh);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) store_out(out, e + c, g[c] / (1.0f + __expf(-g[c])) * u[c], out_dtype);
 }
 
 int cu_count_tiled() {
@@ -333,15 +384,20 @@ TiledGeometry tiled_geometry(int M, int K, int N) {
   return best;
 }
 
+template <int ACT, int GPC, class T, bool GLU>
+hipError_t launch_glu(const GemmArgs& a, const TiledParams& p, dim3 grid) {
+  if (a.nf4)
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+  else if (a.qzeros)
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+  else
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+  return hipGetLastError();
+}
+
 template <int ACT, int GPC, class T>
 hipError_t launch_fmt(const GemmArgs& a, const TiledParams& p, dim3 grid) {
-  if (a.nf4)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4, T>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
-  else if (a.qzeros)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
-  else
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
-  return hipGetLastError();
+  return a.glu ? launch_glu<ACT, GPC, T, true>(a, p, grid) : launch_glu<ACT, GPC, T, false>(a, p, grid);
 }
 
 template <int ACT, class T>
@@ -394,12 +450,20 @@ hipError_t launch_tiled(const GemmArgs& a) {
   p.S = g.S;
   p.kps = g.kps;
   p.partials = g.S > 1 ? static_cast<float*>(a.workspace) : nullptr;
+  p.half = p.NT / 2;
   const dim3 grid(g.tiles_m * g.tiles_n, g.S);
   const hipError_t e = g.small ? launch_act<SmallTile>(a, p, grid) : launch_act<LargeTile>(a, p, grid);
   if (e != hipSuccess || g.S == 1) return e;
-  const size_t quads = (size_t)a.M * a.N / 4;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, a.stream,
-                     p.partials, a.M, a.N, g.S, (size_t)g.tiles_m * g.bm * a.N, a.out, a.out_dtype);
+  const size_t slice_stride = (size_t)g.tiles_m * g.bm * a.N;
+  if (a.glu) {
+    const size_t quads = (size_t)a.M * (a.N / 2) / 4;
+    hipLaunchKernelGGL(splitk_reduce_glu_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                       a.stream, p.partials, a.M, a.N / 2, g.S, slice_stride, a.out, a.out_dtype);
+  } else {
+    const size_t quads = (size_t)a.M * a.N / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                       a.stream, p.partials, a.M, a.N, g.S, slice_stride, a.out, a.out_dtype);
+  }
   return hipGetLastError();
 }
 
