@@ -19,6 +19,7 @@ Modules
   dequant   codes + scales (+ zeros | codebook) -> 16-bit weight matrix
   gemm      dequantize-then-matmul reference (fp64) and a brute-force loop version
   glu       SwiGLU epilogue of a fused gate+up projection, and its parity bound
+  gptq      GPTQ: row-by-row quantization with inverse-Hessian error compensation
   storage   bytes and bits per weight of the packed format
   roofline  memory/compute floors and the batch crossover
 
@@ -34,6 +35,7 @@ from .packing import pack_codes, unpack_codes, pack_zeros, unpack_zeros
 from .dequant import dequant_affine, dequant_sym, dequant_nf4
 from .gemm import gemm_ref, gemm_ref_columns, gemm_bruteforce
 from .glu import silu, swiglu_split, swiglu_ref, swiglu_bound
+from .gptq import hessian, compensate, gptq_quantize
 from .storage import storage_bytes, bits_per_weight, bytes_per_weight
 from . import roofline
 
@@ -46,5 +48,6 @@ __all__ = [
     "dequant_affine", "dequant_sym", "dequant_nf4",
     "gemm_ref", "gemm_ref_columns", "gemm_bruteforce",
     "silu", "swiglu_split", "swiglu_ref", "swiglu_bound",
+    "hessian", "compensate", "gptq_quantize",
     "storage_bytes", "bits_per_weight", "bytes_per_weight", "roofline",
 ]

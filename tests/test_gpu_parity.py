@@ -205,6 +205,38 @@ def test_swiglu_rejects_odd_strip_halves():
         run_swiglu(c, d)
 
 
+@pytest.mark.parametrize("M,K,N,g,sym", [(1, 512, 256, 128, False), (8, 1024, 128, 32, True),
+                                         (96, 512, 192, 64, False)])
+def test_gptq_codes_end_to_end(M, K, N, g, sym):
+    """Weights quantized by the oracle's GPTQ on correlated calibration inputs run through the
+    same kernels: parity with the oracle GEMM, and on the calibration rows the GPU output is
+    closer to x W than the RTN weights' GPU output ("4.3 Weight-only INT4", section 2.1)."""
+    torch = torch_mod()
+    _announce(f"gptq M={M} K={K} N={N} g={g} sym={sym}")
+    rng = np.random.default_rng(M + K)
+    W = synth.gaussian_weight(K, N, 90 + M)
+    C = 0.9 ** np.abs(np.subtract.outer(np.arange(K), np.arange(K)))
+    X = rng.normal(0, 1, (max(4 * K, 256), K)) @ np.linalg.cholesky(C).T
+    x = X[:M].astype(np.float16)
+    errs = []
+    for quant in ("gptq", "rtn"):
+        if sym:
+            q, s = (oracle.gptq_quantize(W, X, g, symmetric=True) if quant == "gptq"
+                    else oracle.quantize_rtn_sym(W, g))
+            qw, qz = oracle.pack_codes(oracle.to_offset_binary(q)), None
+            w_hat = oracle.dequant_sym(qw, s, g)
+        else:
+            q, s, z = oracle.gptq_quantize(W, X, g) if quant == "gptq" else oracle.quantize_rtn_asym(W, g)
+            qw, qz = oracle.pack_codes(q), oracle.pack_zeros(z)
+            w_hat = oracle.dequant_affine(qw, s, qz, g)
+        c = {"M": M, "K": K, "N": N, "g": g, "act": "f16", "x": x, "nf4": False,
+             "qweight": qw, "scales": s, "qzeros": qz}
+        y = from_dev(run_gemm(c, device_inputs(c), out_dtype=torch.float32)).astype(np.float64)
+        assert_close(y, oracle.gemm_ref(x, w_hat), f"{quant} codes")
+        errs.append(np.linalg.norm(y - x.astype(np.float64) @ W))
+    assert errs[0] < errs[1], f"GPTQ output error {errs[0]:.4g} not below RTN {errs[1]:.4g}"
+
+
 def test_gemm_m0_is_noop():
     import weight_only_int4_w4a16_amd as w4
     torch = torch_mod()

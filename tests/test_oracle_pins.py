@@ -360,6 +360,86 @@ def test_swiglu_bound_covers_first_order_perturbation():
         assert np.abs(dh).max() <= bound
 
 
+# ---------------------------------------------------------------- GPTQ
+
+
+def test_gptq_pages_two_weight_example():
+    # two nearly identical input columns: fixing w1 = 0.26 at 0.30 (0.04 over) moves the still
+    # free w2 down by about 0.04 and leaves the output almost unchanged; with orthogonal
+    # columns nothing moves ("4.3 Weight-only INT4", section 2.2)
+    rng = np.random.default_rng(3)
+    x1 = rng.normal(0, 1, 512)
+    w = np.array([[0.26], [0.50]])
+    for x2, expect in ((x1 + 1e-3 * rng.normal(0, 1, 512), -0.04), (None, 0.0)):
+        if x2 is None:
+            X = np.zeros((512, 2))
+            X[:256, 0] = x1[:256]
+            X[256:, 1] = x1[256:]
+        else:
+            X = np.stack([x1, x2], axis=1)
+        Hinv = np.linalg.inv(oracle.hessian(X, damp=0.0))
+        W_new, Hinv_next = oracle.compensate(w, np.array([0.30]), Hinv)
+        assert W_new[0, 0] == 0.30
+        assert abs((W_new[1, 0] - 0.50) - expect) < 1e-3
+        assert Hinv_next.shape == (1, 1)
+        if x2 is not None:
+            # the output moved far less than the 0.04 overshoot alone would move it
+            moved = np.linalg.norm(X @ (W_new - w)) / np.linalg.norm(x1)
+            assert moved < 0.02 * 0.04
+
+
+def test_gptq_with_uncorrelated_inputs_is_rtn():
+    # diagonal H: no compensation reaches another row, so the codes are the RTN codes
+    rng = np.random.default_rng(4)
+    K, N = 64, 24
+    W = rng.normal(0, 0.02, (K, N))
+    X = np.diag(rng.uniform(0.5, 2.0, K))
+    q, s, z = oracle.gptq_quantize(W, X, 32)
+    qr, sr, zr = oracle.quantize_rtn_asym(W, 32)
+    assert np.array_equal(q, qr) and np.array_equal(s, sr) and np.array_equal(z, zr)
+    qs, ss = oracle.gptq_quantize(W, X, 32, symmetric=True)
+    qsr, ssr = oracle.quantize_rtn_sym(W, 32)
+    assert np.array_equal(qs, qsr) and np.array_equal(ss, ssr)
+
+
+def _correlated_inputs(rng, n, K, rho=0.9):
+    C = rho ** np.abs(np.subtract.outer(np.arange(K), np.arange(K)))
+    return rng.normal(0, 1, (n, K)) @ np.linalg.cholesky(C).T
+
+
+@pytest.mark.parametrize("sym", [False, True])
+def test_gptq_lowers_the_output_error_against_rtn(sym):
+    # the objective of section 2.1: ||X W - X W_hat|| on the calibration inputs
+    rng = np.random.default_rng(7 + sym)
+    K, N, g = 128, 32, 32
+    W = rng.normal(0, 0.02, (K, N))
+    X = _correlated_inputs(rng, 512, K)
+    if sym:
+        q, s = oracle.gptq_quantize(W, X, g, symmetric=True)
+        qr, sr = oracle.quantize_rtn_sym(W, g)
+        wh = oracle.dequant_sym(oracle.pack_codes(oracle.to_offset_binary(q)), s, g)
+        whr = oracle.dequant_sym(oracle.pack_codes(oracle.to_offset_binary(qr)), sr, g)
+    else:
+        q, s, z = oracle.gptq_quantize(W, X, g)
+        qr, sr, zr = oracle.quantize_rtn_asym(W, g)
+        wh = oracle.dequant_affine(oracle.pack_codes(q), s, oracle.pack_zeros(z), g)
+        whr = oracle.dequant_affine(oracle.pack_codes(qr), sr, oracle.pack_zeros(zr), g)
+    e_gptq = np.linalg.norm(X @ (W - wh.astype(np.float64)))
+    e_rtn = np.linalg.norm(X @ (W - whr.astype(np.float64)))
+    assert e_gptq < 0.7 * e_rtn
+
+
+def test_gptq_inverse_update_equals_direct_inverse():
+    rng = np.random.default_rng(8)
+    K, N = 64, 8
+    W = rng.normal(0, 0.02, (K, N))
+    X = _correlated_inputs(rng, 256, K)
+    a = oracle.gptq_quantize(W, X, 32, scale_dtype="bf16")
+    b = oracle.gptq_quantize(W, X, 32, scale_dtype="bf16", exact_inverse=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
 # ---------------------------------------------------------------- NF4
 
 def test_inverse_normal_matches_library():
