@@ -20,6 +20,7 @@ Modules
   gemm      dequantize-then-matmul reference (fp64) and a brute-force loop version
   glu       SwiGLU epilogue of a fused gate+up projection, and its parity bound
   gptq      GPTQ: row-by-row quantization with inverse-Hessian error compensation
+  awq       AWQ: per-input-channel scale search, S W quantized, activations times S^-1
   storage   bytes and bits per weight of the packed format
   roofline  memory/compute floors and the batch crossover
 
@@ -36,6 +37,7 @@ from .dequant import dequant_affine, dequant_sym, dequant_nf4
 from .gemm import gemm_ref, gemm_ref_columns, gemm_bruteforce
 from .glu import silu, swiglu_split, swiglu_ref, swiglu_bound
 from .gptq import hessian, compensate, gptq_quantize
+from . import awq
 from .storage import storage_bytes, bits_per_weight, bytes_per_weight
 from . import roofline
 
@@ -48,6 +50,6 @@ __all__ = [
     "dequant_affine", "dequant_sym", "dequant_nf4",
     "gemm_ref", "gemm_ref_columns", "gemm_bruteforce",
     "silu", "swiglu_split", "swiglu_ref", "swiglu_bound",
-    "hessian", "compensate", "gptq_quantize",
+    "hessian", "compensate", "gptq_quantize", "awq",
     "storage_bytes", "bits_per_weight", "bytes_per_weight", "roofline",
 ]

@@ -440,6 +440,107 @@ def test_gptq_inverse_update_equals_direct_inverse():
         assert np.array_equal(u, v)
 
 
+# ---------------------------------------------------------------- AWQ
+
+def test_awq_scaled_activation_rounding_hand_worked():
+    # fp16 in [2, 4) has a step of 2/1024. 3 * 1025/1024 = 3 + 1.5 steps: a tie between an
+    # odd (1 step) and an even (2 steps) significand -> 3 + 4/1024. 3 * 1027/1024 = 3 + 4.5
+    # steps -> the even 4 steps, 3 + 8/1024 (truncation would give the first 3 + 2/1024,
+    # round-half-up the second 3 + 10/1024). A power of two is exact.
+    x = np.array([[3.0, 3.0, 1.5, -0.75]], dtype=np.float16)
+    s = np.array([1025 / 1024, 1027 / 1024, 0.5, 4.0], dtype=np.float16)
+    got = oracle.awq.scale_activations(x, s, "f16").astype(np.float64)
+    assert got.tolist() == [[3 + 4 / 1024, 3 + 8 / 1024, 0.75, -3.0]]
+    # bf16 in [2, 4) has a step of 2/128: 3 * (1 + 1/128) = 3 + 1.5 steps -> 3 + 4/128
+    xb = oracle.round_nearest_bf16_bits(np.array([[3.0, -5.0]]))
+    sb = oracle.round_nearest_bf16_bits(np.array([1 + 1 / 128, 0.25]))
+    gotb = oracle.bf16_bits_to_f64(oracle.awq.scale_activations(xb, sb, "bf16"))
+    assert gotb.tolist() == [[3 + 4 / 128, -1.25]]
+
+
+def test_awq_scaling_is_an_identity_before_quantization():
+    # section 3.2: Y = (X S^-1)(S W). S scales the rows of W (input channels), so a slip to
+    # columns, or S instead of S^-1 on one side, breaks the identity.
+    rng = np.random.default_rng(21)
+    K, N = 48, 24
+    W = rng.normal(0, 1, (K, N))
+    X = rng.normal(0, 1, (16, K))
+    s_inv = oracle.round_nearest_f16(rng.uniform(0.2, 5.0, K))
+    SW = oracle.awq.scale_weight(W, s_inv)
+    XS = X * s_inv.astype(np.float64)[None, :]
+    assert np.allclose(XS @ SW, X @ W, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(XS @ (W * (1.0 / s_inv.astype(np.float64))[None, :N]), X @ W)
+
+
+def test_awq_alpha_zero_is_rtn_and_scales_normalised():
+    rng = np.random.default_rng(22)
+    K, N, g = 64, 16, 32
+    W = rng.normal(0, 0.05, (K, N))
+    X = rng.normal(0, 1, (128, K)) * rng.uniform(0.1, 10.0, K)[None, :]
+    assert np.all(oracle.awq.candidate_scales(X, 0.0) == np.float16(1.0))
+    quant, s_inv, alpha, errs = oracle.awq.awq_quantize(W, X, g, n_grid=1)
+    assert alpha == 0.0
+    for u, v in zip(quant, oracle.quantize_rtn_asym(W, g)):
+        assert np.array_equal(u, v)
+    # errs[0] is RTN's output error, computed here through the plain GEMM oracle
+    q, s, z = oracle.quantize_rtn_asym(W, g)
+    wh = oracle.dequant_affine(oracle.pack_codes(q), s, oracle.pack_zeros(z), g)
+    X16 = oracle.round_nearest_f16(X)
+    e = np.sum((oracle.gemm_ref(X16, W, "f64") - oracle.gemm_ref(X16, wh)) ** 2)
+    assert errs[0] == pytest.approx(e, rel=1e-12)
+    # s = a ** alpha with max(s) min(s) = 1; larger mean |x| -> larger s -> smaller s_inv
+    a = np.mean(np.abs(X), axis=0)
+    sv = 1.0 / oracle.awq.candidate_scales(X, 0.5).astype(np.float64)
+    assert sv.max() * sv.min() == pytest.approx(1.0, rel=2e-3)
+    order = np.argsort(a)
+    assert np.all(np.diff(sv[order]) >= -1e-3 * sv[order][1:])
+    assert sv[order[-1]] / sv[order[0]] == pytest.approx(np.sqrt(a.max() / a.min()), rel=2e-3)
+
+
+def test_awq_amplified_weight_has_a_smaller_effective_error():
+    # section 3.2: with the group's step unchanged, a weight scaled by s before rounding and
+    # divided by s after has at most half a step / s of error. The group's range is fixed
+    # by two other weights (-1 and 1), so scaling the third by 2 leaves the step alone.
+    rng = np.random.default_rng(23)
+    w = rng.uniform(-0.45, 0.45, 4000)
+    errs = {}
+    for s in (1.0, 2.0):
+        W = np.stack([np.full_like(w, -1.0), np.full_like(w, 1.0), s * w, np.zeros_like(w)])
+        q, sc, z = oracle.quantize_rtn_asym(W, 4, None)
+        step = sc[0]
+        assert np.allclose(step, 2.0 / 15)
+        w_hat = (q[2].astype(np.float64) - z[0]) * step
+        errs[s] = np.abs(w_hat / s - w)
+        assert np.all(errs[s] <= step / (2 * s) + 1e-12)
+    assert errs[1.0].max() > 0.9 * (2.0 / 15) / 2
+    assert errs[2.0].mean() < 0.6 * errs[1.0].mean()
+
+
+@pytest.mark.parametrize("sym,dt", [(False, "f16"), (True, "bf16")])
+def test_awq_lowers_the_output_error_against_rtn(sym, dt):
+    # section 3.1: the channels with large activations carry the error; protecting them by
+    # scaling (3.2) beats RTN on inputs where 1/32 of the channels run 10x larger
+    rng = np.random.default_rng(24 + sym)
+    K, N, g = 256, 64, 64
+    X = rng.normal(0, 1, (256, K))
+    X[:, rng.choice(K, K // 32, replace=False)] *= 10.0
+    W = rng.normal(0, 0.05, (K, N))
+    quant, s_inv, alpha, errs = oracle.awq.awq_quantize(W, X, g, dt, sym)
+    assert alpha > 0 and min(errs) == errs[int(round(alpha * 20))]
+    assert min(errs) < 0.7 * errs[0]
+    # the returned codes reproduce the chosen error through the plain dequant + GEMM oracle
+    if sym:
+        q, s = quant
+        wh = oracle.dequant_sym(oracle.pack_codes(oracle.to_offset_binary(q)), s, g, dt)
+    else:
+        q, s, z = quant
+        wh = oracle.dequant_affine(oracle.pack_codes(q), s, oracle.pack_zeros(z), g, dt)
+    Xq = oracle.round_nearest_f16(X) if dt == "f16" else oracle.round_nearest_bf16_bits(X)
+    y = oracle.gemm_ref(oracle.awq.scale_activations(Xq, s_inv, dt), wh, dt)
+    y0 = (Xq.astype(np.float64) if dt == "f16" else oracle.bf16_bits_to_f64(Xq)) @ W
+    assert np.sum((y - y0) ** 2) == pytest.approx(min(errs), rel=1e-9)
+
+
 # ---------------------------------------------------------------- NF4
 
 def test_inverse_normal_matches_library():
