@@ -295,6 +295,71 @@ def sweep(args, torch, w4) -> int:
     return 0
 
 
+def _graph_us(torch, fn, steps: int) -> float:
+    """us per replay of a HIP graph capturing fn (3 warm-up replays, then steps timed)."""
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def awq(args, torch, w4) -> int:
+    """AWQ-scaled GEMM (w4a16_gemm_awq) against the plain GEMM on the same weights: the 8B
+    decode linears at M=1 and 16 (32 distinct weights per shape, so they stream from HBM),
+    the crossover shape at M=256 and the prefill shape. One JSON line per shape and M."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261205)
+    g = 128
+    cases = [(M, K, N, torch.float16, 32) for M in (1, 16)
+             for (K, N) in ((4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096))]
+    cases += [(256, 4096, 14336, torch.float16, 32), (2048, 8192, 28672, torch.bfloat16, 4)]
+    for (M, K, N, dt, copies) in cases:
+        ws_ = []
+        for _ in range(copies):
+            qw = torch.randint(-2**31, 2**31 - 1, (K // 8, N), dtype=torch.int32, device=dev,
+                               generator=gen)
+            sc = (torch.rand((K // g, N), device=dev, generator=gen) * 0.005 + 0.004).to(dt)
+            qz = torch.randint(-2**31, 2**31 - 1, (K // g, N // 8), dtype=torch.int32, device=dev,
+                               generator=gen)
+            ws_.append((w4.pack(qw), sc, qz))
+        x = torch.randn((M, K), device=dev, generator=gen).to(dt)
+        s_inv = torch.exp2(torch.rand(K, device=dev, generator=gen) * 4 - 2).to(dt)
+        y = torch.empty((M, N), device=dev, dtype=dt)
+        ws = torch.empty(max(w4.awq_workspace_bytes(M, K, N, g), 256), dtype=torch.uint8, device=dev)
+
+        def plain():
+            for w in ws_:
+                w4.gemm(x, *w, g, out=y, workspace=ws)
+
+        def scaled():
+            for w in ws_:
+                w4.gemm_awq(x, s_inv, *w, g, out=y, workspace=ws)
+
+        res = {k: round(_graph_us(torch, fn, args.steps) / copies, 2)
+               for k, fn in (("plain_us", plain), ("awq_us", scaled))}
+        res["awq_over_plain"] = round(res["awq_us"] / res["plain_us"], 3)
+        print(json.dumps({"config": "awq", "M": M, "K": K, "N": N, "dtype": str(dt).split(".")[-1],
+                          "kernel": w4.kernel_name(M, K, N, g),
+                          "awq_workspace": w4.awq_workspace_bytes(M, K, N, g), **res}), flush=True)
+        del ws_
+        torch.cuda.empty_cache()
+    return 0
+
+
 def mlp(args, torch, w4) -> int:
     """The Llama-3-8B-shaped decode MLP per layer (32 layers of distinct weights, asymmetric
     g128, fp16), replayed from a HIP graph: the fused path is w4a16_gemm_swiglu on the
@@ -338,23 +403,7 @@ def mlp(args, torch, w4) -> int:
 
         res = {}
         for name, fn in (("fused_us", fused), ("unfused_us", unfused)):
-            fn()
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                fn()
-            for _ in range(3):
-                graph.replay()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(args.steps):
-                graph.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            res[name] = round(e0.elapsed_time(e1) * 1e3 / (args.steps * len(layers)), 2)
-            del graph
+            res[name] = round(_graph_us(torch, fn, args.steps) / len(layers), 2)
         res["speedup"] = round(res["unfused_us"] / res["fused_us"], 3)
         print(json.dumps({"config": "mlp llama3-8b (gate+up 4096x28672 with SwiGLU, down 14336x4096)",
                           "M": M, "swiglu_kernel": w4.kernel_name(M, K, N2, g), **res}), flush=True)
@@ -372,6 +421,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a HIP graph")
     ap.add_argument("--mlp", action="store_true",
                     help="time the fused SwiGLU decode MLP against the unfused path, per layer")
+    ap.add_argument("--awq", action="store_true",
+                    help="time the AWQ-scaled GEMM against the plain GEMM on the same weights")
     ap.add_argument("--sweep", action="store_true",
                     help="per-(config, shape, M) timing table of every benchmark config, one JSON "
                          "line per row, instead of the step benchmark")
@@ -402,6 +453,8 @@ def main() -> int:
 
     if args.mlp:
         return mlp(args, torch, w4)
+    if args.awq:
+        return awq(args, torch, w4)
     if args.sweep:
         return sweep(args, torch, w4)
 

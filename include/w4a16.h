@@ -119,6 +119,30 @@ w4a16_status w4a16_gemm_swiglu(const void* x, int M, int K, int N2, w4a16_dtype 
                                int group_size, void* out, w4a16_dtype out_dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Bytes of scratch device memory w4a16_gemm_awq needs for this shape on the current device:
+ * as w4a16_workspace_bytes, except for decode shapes (M <= 16) whose activations do not fit
+ * the kernel's LDS staging, which get min(M, 16) * K * 2 bytes (256-byte multiple) for the
+ * scaled activations. Returns 0 for bad shapes. */
+size_t w4a16_awq_workspace_bytes(int M, int K, int N, int group_size);
+
+/* The W4A16 GEMM of AWQ-scaled activations ("4.3 Weight-only INT4", section 3.2: the weight
+ * is deployed as the regular INT4 format of S W, and the product is Y_hat = (X S^-1) D(Q(S W))
+ * with S = diag(s) one factor per input channel):
+ *   y = x' @ W_hat,  x'[m][k] = RN_act(x[m][k] * s_inv[k])
+ * one round-to-nearest-even of the exact product of two act values, formed as x is staged
+ * for the MFMAs (decode shapes whose x does not fit in LDS: by a first small kernel into the
+ * workspace).
+ *   s_inv     [in]  act [K], the per-input-channel S^-1, 16-byte aligned
+ *   workspace [in/out] >= w4a16_awq_workspace_bytes(M, K, N, group_size) bytes, 256-byte
+ *                   aligned (may be NULL when that size is 0)
+ * Other arguments, errors and determinism as for w4a16_gemm (s_inv NULL with M > 0, or
+ * misaligned: W4A16_ERR_ARG). */
+w4a16_status w4a16_gemm_awq(const void* x, const void* s_inv, int M, int K, int N,
+                            w4a16_dtype act, const int32_t* packed, const void* scales,
+                            const int32_t* qzeros, int group_size, void* out,
+                            w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* NF4 counterpart of w4a16_gemm_swiglu (absmax [K/block_size][N2] fp16, codebook as for
  * w4a16_gemm_nf4). */
 w4a16_status w4a16_gemm_nf4_swiglu(const void* x, int M, int K, int N2, w4a16_dtype act,

@@ -26,6 +26,7 @@ def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for n in ("w4a16_pack", "w4a16_gemm", "w4a16_gemm_nf4", "w4a16_dequant",
               "w4a16_dequant_nf4", "w4a16_packed_bytes", "w4a16_workspace_bytes", "w4a16_kernel_name",
+              "w4a16_gemm_awq", "w4a16_awq_workspace_bytes", "w4a16_gemm_swiglu",
               "w4a16_status_string", "w4a16_version"):
         assert n in names
 
@@ -89,6 +90,26 @@ def test_workspace_bytes(L):
     assert workspace_bytes(2048, 8192, 28672, 128) == 0
     assert workspace_bytes(200, 2048, 64, 128) == 8 * 256 * 64 * 4    # 8 slices of 2 k-blocks
     assert workspace_bytes(32, 4096, 28672, 128) == 2 * 64 * 28672 * 4
+
+
+def test_awq_rejects_bad_s_inv_and_sizes_its_workspace(L):
+    from weight_only_int4_w4a16_amd import awq_workspace_bytes, workspace_bytes
+    vp = ctypes.c_void_p
+    for s_inv in (None, vp(18)):                       # missing, or not 16-byte aligned
+        st = L.w4a16_gemm_awq(vp(16), s_inv, 1, 4096, 4096, 0, vp(16), vp(16), vp(16), 128,
+                              vp(16), 0, vp(256), 1 << 30, None)
+        assert st == 1
+    assert L.w4a16_gemm_awq(None, None, 0, 4096, 4096, 0, None, None, None, 128, None, 0,
+                            None, 0, None) == 0        # M = 0 is a no-op
+    # decode shapes whose x fits in LDS (rows * K * 2 <= 128 KiB) need nothing; the others
+    # get rows * K * 2 bytes for the scaled activations; batched shapes as the plain GEMM
+    assert awq_workspace_bytes(1, 14336, 4096, 128) == 0
+    assert awq_workspace_bytes(16, 4096, 28672, 128) == 0
+    assert awq_workspace_bytes(8, 14336, 4096, 128) == 8 * 14336 * 2
+    assert awq_workspace_bytes(16, 14336, 4096, 128) == 16 * 14336 * 2
+    assert awq_workspace_bytes(9, 9216, 256, 128) == 9 * 9216 * 2
+    assert awq_workspace_bytes(200, 2048, 64, 128) == workspace_bytes(200, 2048, 64, 128) > 0
+    assert awq_workspace_bytes(16, 4096, 4104, 128) == 0   # N % 16: no shape
 
 
 def test_nf4_requires_codebook(L):

@@ -46,6 +46,10 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemm.restype = i32
     L.w4a16_gemm_nf4.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
     L.w4a16_gemm_nf4.restype = i32
+    L.w4a16_awq_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.w4a16_awq_workspace_bytes.restype = sz
+    L.w4a16_gemm_awq.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
+    L.w4a16_gemm_awq.restype = i32
     L.w4a16_gemm_swiglu.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
     L.w4a16_gemm_swiglu.restype = i32
     L.w4a16_gemm_nf4_swiglu.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
@@ -102,6 +106,10 @@ def packed_bytes(K: int, N: int) -> int:
 
 def workspace_bytes(M: int, K: int, N: int, group_size: int) -> int:
     return int(lib().w4a16_workspace_bytes(M, K, N, group_size))
+
+
+def awq_workspace_bytes(M: int, K: int, N: int, group_size: int) -> int:
+    return int(lib().w4a16_awq_workspace_bytes(M, K, N, group_size))
 
 
 def _workspace(device, nbytes: int, workspace=None):
@@ -180,6 +188,30 @@ def gemm_nf4(x, packed, absmax, codebook, block_size: int = 64, out_dtype=None, 
                               _ptr(codebook), block_size, _ptr(out), _dt(out.dtype), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size(), _stream(x))
     _check(st, "w4a16_gemm_nf4")
+    return out
+
+
+def gemm_awq(x, s_inv, packed, scales, qzeros, group_size: int, out_dtype=None, out=None,
+             workspace=None):
+    """``y = RN(x * s_inv) @ W_hat``: the GEMM of AWQ-scaled activations, ``s_inv[K]`` the
+    per-input-channel S^-1 in x's dtype, the weight the INT4 format of S W (as for
+    :func:`gemm`). ``workspace``: optional, ``awq_workspace_bytes(M, K, N, group_size)``."""
+    torch = _torch()
+    M, K = x.shape
+    N = scales.shape[1]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if scales.dtype != x.dtype or s_inv.dtype != x.dtype:
+        raise W4A16Error("scales and s_inv must have the activation dtype")
+    if s_inv.shape != (K,) or not s_inv.is_contiguous():
+        raise W4A16Error("s_inv must be a contiguous (K,) tensor")
+    ws = _workspace(x.device, awq_workspace_bytes(M, K, N, group_size) if M else 0, workspace)
+    st = lib().w4a16_gemm_awq(_ptr(x), _ptr(s_inv), M, K, N, _dt(x.dtype), _ptr(packed),
+                              _ptr(scales), _ptr(qzeros), group_size, _ptr(out), _dt(out.dtype),
+                              _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(x))
+    _check(st, "w4a16_gemm_awq")
     return out
 
 

@@ -36,6 +36,14 @@ size_t workspace_need(int M, int K, int N, int gs) {
   return w4a16::decode_config(M < 16 ? M : 16, K, N, gs, false).workspace_bytes;
 }
 
+// AWQ-scaled x: decode launches whose x does not fit in LDS scale it into the workspace first
+size_t awq_workspace_need(int M, int K, int N, int gs) {
+  GemmArgs a{};
+  a.M = M; a.K = K; a.N = N; a.group_size = gs;
+  if (use_tiled(a)) return w4a16::tiled_workspace_bytes(M, K, N);
+  return w4a16::decode_awq_workspace_bytes(M < 16 ? M : 16, K, N, gs);
+}
+
 w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
   if (a.M < 0) return W4A16_ERR_ARG;
   w4a16_status st = check_shape(a.K, a.N, a.group_size);
@@ -49,9 +57,11 @@ w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
   if (!aligned(a.x, 16) || !aligned(a.packed, 16) || !aligned(a.out, 16)) return W4A16_ERR_ARG;
   if (!aligned(a.scales, 2) || (a.qzeros && !aligned(a.qzeros, 4))) return W4A16_ERR_ARG;
   if (a.codebook && !aligned(a.codebook, 2)) return W4A16_ERR_ARG;
+  if (a.xscale && !aligned(a.xscale, 16)) return W4A16_ERR_ARG;
   a.act = act == W4A16_F16 ? w4a16::ACT_F16 : w4a16::ACT_BF16;
   a.out_dtype = (int)out_dtype;
-  const size_t need = workspace_need(a.M, a.K, a.N, a.group_size);
+  const size_t need = a.xscale ? awq_workspace_need(a.M, a.K, a.N, a.group_size)
+                               : workspace_need(a.M, a.K, a.N, a.group_size);
   if (need && (!a.workspace || !aligned(a.workspace, 256) || a.workspace_bytes < need))
     return W4A16_ERR_WORKSPACE;
   if (use_tiled(a)) return from_hip(w4a16::launch_tiled(a));
@@ -89,6 +99,32 @@ w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
                         size_t workspace_bytes, void* stream) {
   GemmArgs a{};
   a.x = x; a.M = M; a.K = K; a.N = N;
+  a.packed = reinterpret_cast<const uint32_t*>(packed);
+  a.scales = scales;
+  a.qzeros = reinterpret_cast<const uint32_t*>(qzeros);
+  a.codebook = nullptr; a.nf4 = false;
+  a.group_size = group_size;
+  a.out = out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.stream = static_cast<hipStream_t>(stream);
+  return gemm_common(a, act, out_dtype);
+}
+
+size_t w4a16_awq_workspace_bytes(int M, int K, int N, int group_size) {
+  if (M < 0 || check_shape(K, N, group_size) != W4A16_OK) return 0;
+  if (M == 0) return 0;
+  return awq_workspace_need(M, K, N, group_size);
+}
+
+w4a16_status w4a16_gemm_awq(const void* x, const void* s_inv, int M, int K, int N,
+                            w4a16_dtype act, const int32_t* packed, const void* scales,
+                            const int32_t* qzeros, int group_size, void* out,
+                            w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (M > 0 && !s_inv) return W4A16_ERR_ARG;
+  GemmArgs a{};
+  a.x = x; a.M = M; a.K = K; a.N = N;
+  a.xscale = s_inv;
   a.packed = reinterpret_cast<const uint32_t*>(packed);
   a.scales = scales;
   a.qzeros = reinterpret_cast<const uint32_t*>(qzeros);

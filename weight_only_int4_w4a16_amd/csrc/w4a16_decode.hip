@@ -127,6 +127,22 @@ DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu) {
   return choose(M, K, N, group_size, false, glu);
 }
 
+namespace {
+
+// AWQ input scaling for launches whose x does not fit in LDS: x' = RN(x * s_inv[k]) written
+// to the workspace, one 16-byte chunk (8 activations) per thread, then the plain kernel.
+template <int ACT>
+__global__ __launch_bounds__(256) void awq_scale_kernel(const u4_t* __restrict__ x,
+                                                        const u4_t* __restrict__ s_inv, int K8,
+                                                        int chunks, u4_t* __restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < chunks) out[i] = scale_act8<ACT>(x[i], s_inv[i % K8]);
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
 // Rows of x one launch takes: at most 16, one MFMA tile (larger M goes to the batched
 // kernel; a caller of this launcher with more rows gets several launches).
 DecodeConfig decode_launch_config(int M, int K, int N, int group_size, bool glu) {
@@ -140,6 +156,11 @@ const char* decode_name(int M, int K, int N, int group_size, int act) {
   return c.SW == 1 ? "w4a16_decode_sw1" : "w4a16_decode_sw2";
 }
 
+size_t decode_awq_workspace_bytes(int M, int K, int N, int group_size) {
+  const DecodeConfig c = decode_launch_config(M, K, N, group_size, false);
+  return c.x_in_lds ? 0 : align256((size_t)c.rows * K * 2);
+}
+
 hipError_t launch_decode(const GemmArgs& a) {
   const size_t osz = a.out_dtype == 2 ? 4 : 2;
   for (int r0 = 0; r0 < a.M;) {
@@ -147,6 +168,19 @@ hipError_t launch_decode(const GemmArgs& a) {
     const int rows = c.rows;
     DecodeParams p;
     p.x = static_cast<const uint16_t*>(a.x) + (size_t)r0 * a.K;
+    p.xscale = nullptr;
+    if (a.xscale && c.x_in_lds) {
+      p.xscale = static_cast<const uint16_t*>(a.xscale);
+    } else if (a.xscale) {  // x' to the workspace (launches run in order on the stream)
+      const int chunks = rows * (a.K / 8);
+      hipLaunchKernelGGL(a.act == ACT_F16 ? awq_scale_kernel<ACT_F16> : awq_scale_kernel<ACT_BF16>,
+                         dim3(ceil_div(chunks, 256)), dim3(256), 0, a.stream,
+                         reinterpret_cast<const u4_t*>(p.x), static_cast<const u4_t*>(a.xscale),
+                         a.K / 8, chunks, static_cast<u4_t*>(a.workspace));
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      p.x = static_cast<const uint16_t*>(a.workspace);
+    }
     p.M = rows;
     p.K = a.K;
     p.N = a.N;

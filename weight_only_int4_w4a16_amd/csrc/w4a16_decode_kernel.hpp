@@ -60,6 +60,7 @@ struct DecodeParams {
   int xslice;    // LDS halves reserved per wave for its slice of x (XL)
   int GPC;       // scale groups per 128-k block (128 / group size)
   int half;      // GLU: strips per half of the fused gate+up weight (N / 32)
+  const uint16_t* xscale;  // XS: AWQ S^-1 [K] in the activation type
 };
 
 constexpr int kXRegs = 2;  // 16-byte chunks of x per lane staged in registers ahead of the weights
@@ -98,10 +99,12 @@ __device__ __forceinline__ int tile_of(int b, int G) {
 // over tiles blockIdx.x, + gridDim.x, ... with x staged once.
 // GLU: the weight is a fused gate+up projection [K][2 Nh] (gate columns first); tile t pairs
 // gate strip t with up strip t + Nh/16 and stores h = SiLU(gate) * up, [M][Nh].
-template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, int LB, bool PT, bool GLU>
+// XS (x in LDS only): AWQ input scaling, x' = RN(x * s_inv[k]) as x is staged.
+template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, int LB, bool PT, bool GLU, bool XS>
 __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   typedef typename ActT<ACT>::type AT;
   static_assert(!GLU || SW == 2, "a SwiGLU tile is one gate strip and one up strip");
+  static_assert(!XS || XL, "x is scaled as it is staged in LDS");
   constexpr int D = decode_group_blocks(SW, GPC, XL);  // k-blocks per group
   constexpr int SPG = 4 / GPC;        // 32-k steps per scale group
   constexpr bool ZEROS = FMT == FMT_ASYM;
@@ -276,6 +279,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   const int cpr = (min(kc1 * 128, K) - kbeg) >> 3;  // 16-byte chunks per row of the slice
   const int nchunks = XL ? rows * cpr : 0;
   u4_t xr[kXRegs];
+  u4_t xsr[kXRegs];  // XS: the matching chunks of s_inv
   int xoff[kXRegs];
   auto x_load = [&]() __attribute__((always_inline)) {
     if constexpr (XL) {
@@ -287,18 +291,24 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
         const int m = c / cpr, cc = c - (c / cpr) * cpr;
         xoff[i] = m * p.xstride + cc * 8;
         xr[i] = *reinterpret_cast<const u4_t*>(p.x + (size_t)m * K + kbeg + cc * 8);
+        if constexpr (XS) xsr[i] = *reinterpret_cast<const u4_t*>(p.xscale + kbeg + cc * 8);
       }
     }
   };
   auto x_store = [&]() __attribute__((always_inline)) {
     if constexpr (XL) {
 #pragma unroll
-      for (int i = 0; i < kXRegs; ++i) *reinterpret_cast<u4_t*>(xs + xoff[i]) = xr[i];
+      for (int i = 0; i < kXRegs; ++i) {
+        u4_t v = xr[i];
+        if constexpr (XS) v = scale_act8<ACT>(v, xsr[i]);
+        *reinterpret_cast<u4_t*>(xs + xoff[i]) = v;
+      }
       // chunks beyond the register-staged ones (slices of several rows)
       for (int c = lane + 64 * kXRegs; c < nchunks; c += 64) {
         const int m = c / cpr, cc = c - (c / cpr) * cpr;
-        *reinterpret_cast<u4_t*>(xs + (size_t)m * p.xstride + cc * 8) =
-            *reinterpret_cast<const u4_t*>(p.x + (size_t)m * K + kbeg + cc * 8);
+        u4_t v = *reinterpret_cast<const u4_t*>(p.x + (size_t)m * K + kbeg + cc * 8);
+        if constexpr (XS) v = scale_act8<ACT>(v, *reinterpret_cast<const u4_t*>(p.xscale + kbeg + cc * 8));
+        *reinterpret_cast<u4_t*>(xs + (size_t)m * p.xstride + cc * 8) = v;
       }
     }
   };
@@ -456,18 +466,37 @@ template <int ACT, int FMT>
 hipError_t decode_dispatch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s);
 
 
-template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, bool PT, bool GLU>
+template <int ACT, int MT, int SW, int GPC, int FMT, bool XL, bool PT, bool GLU, bool XS = false>
 hipError_t decode_launch(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
   constexpr int LB = PT ? decode_persistent_threads : decode_block_threads(MT, GPC, XL);
-  hipLaunchKernelGGL((decode_kernel<ACT, MT, SW, GPC, FMT, XL, LB, PT, GLU>), dim3(c.grid),
+  hipLaunchKernelGGL((decode_kernel<ACT, MT, SW, GPC, FMT, XL, LB, PT, GLU, XS>), dim3(c.grid),
                      dim3(64 * c.W), c.lds_bytes, s, p);
   return hipGetLastError();
 }
 
 // The instantiated set (all free of register spills on gfx950): tiles of two strips with x
 // in LDS, one 16-row tile and one scale group per k-block; every other case one strip.
+// AWQ-scaled x (p.xscale set): the plain GEMM shapes with x in LDS, affine formats.
 template <int ACT, int FMT, int MT, bool XL, bool PT>
 hipError_t decode_dispatch_gpc(const DecodeParams& p, const DecodeConfig& c, hipStream_t s) {
+  if (p.xscale) {
+    if constexpr (XL && FMT != FMT_NF4) {
+      if (c.glu) return hipErrorNotSupported;
+      if (c.SW == 2) {
+        if constexpr (MT == 1) {
+          if (p.GPC == 1) return decode_launch<ACT, 1, 2, 1, FMT, true, PT, false, true>(p, c, s);
+        }
+        return hipErrorNotSupported;
+      }
+      if (c.SW != 1) return hipErrorNotSupported;
+      switch (p.GPC) {
+        case 1: return decode_launch<ACT, MT, 1, 1, FMT, XL, PT, false, true>(p, c, s);
+        case 2: return decode_launch<ACT, MT, 1, 2, FMT, XL, PT, false, true>(p, c, s);
+        default: return decode_launch<ACT, MT, 1, 4, FMT, XL, PT, false, true>(p, c, s);
+      }
+    }
+    return hipErrorNotSupported;
+  }
   if (c.glu) {  // gate/up strip pairs, every group size
     if (c.SW != 2) return hipErrorNotSupported;
     switch (p.GPC) {

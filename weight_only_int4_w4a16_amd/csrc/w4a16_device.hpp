@@ -289,6 +289,28 @@ __device__ inline f16v_t mfma32(b8_t a, b8_t b, f16v_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// AWQ input scaling of eight activations ("4.3 Weight-only INT4", section 3.2: the GEMM
+// multiplies X S^-1): x' = RN_t(x * s_inv) per element, both operands of type t. fp16: one
+// IEEE fp16 multiply (nearest-even). bf16: the product of two 8-bit significands is exact
+// in fp32, then one nearest-even conversion.
+template <int ACT>
+__device__ inline u4_t scale_act8(u4_t x, u4_t s) {
+  u4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (ACT == ACT_F16) {
+      r[i] = __builtin_bit_cast(uint32_t, as_h2(x[i]) * as_h2(s[i]));
+    } else {
+      const float lo = __builtin_bit_cast(float, x[i] << 16) * __builtin_bit_cast(float, s[i] << 16);
+      const float hi = __builtin_bit_cast(float, x[i] & 0xFFFF0000u) *
+                       __builtin_bit_cast(float, s[i] & 0xFFFF0000u);
+      r[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+    }
+  }
+  return r;
+}
+
 // fp32 -> output element
 __device__ inline void store_out(void* out, size_t idx, float v, int out_dtype) {
   if (out_dtype == 2) {

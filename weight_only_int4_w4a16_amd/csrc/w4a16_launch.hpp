@@ -21,6 +21,7 @@ struct GemmArgs {
   void* out;
   int out_dtype;           // 0 fp16, 1 bf16, 2 fp32
   bool glu;                // N columns = gate | up halves; out = SiLU(gate) * up, [M][N/2]
+  const void* xscale;      // AWQ: S^-1 [K] in the activation dtype (x' = RN(x * s_inv)), or NULL
   void* workspace;         // scratch for split-K partial tiles (no state between calls)
   size_t workspace_bytes;
   hipStream_t stream;
@@ -52,6 +53,7 @@ hipError_t launch_dequant(const GemmArgs& a);  // writes W_hat [K][N] into a.out
 hipError_t launch_decode(const GemmArgs& a);   // M <= 16 (more rows: several launches)
 hipError_t launch_tiled(const GemmArgs& a);    // M > 16
 size_t tiled_workspace_bytes(int M, int K, int N);
+size_t decode_awq_workspace_bytes(int M, int K, int N, int group_size);  // M <= 16
 const char* decode_name(int M, int K, int N, int group_size, int act);
 const char* tiled_name(int M, int K, int N);
 bool tiled_supported(const GemmArgs& a);

@@ -73,6 +73,7 @@ struct TiledParams {
   int S, kps;          // K slices and k-blocks per slice
   float* partials;     // [S][tiles_m * tile rows][N] fp32 (S > 1)
   int half;            // GLU: strips per half of the fused gate+up weight (NT / 2)
+  const uint16_t* xscale;  // XS: AWQ S^-1 [K] in the activation type
 };
 
 // workgroup -> output tile, so that tiles sharing weight columns run on the same XCD
@@ -85,7 +86,8 @@ __device__ __forceinline__ int tile_of(int b, int G) {
 // first strip pair is two gate strips, its second the matching up strips, and the output is
 // h = SiLU(gate) * up, [M][Nh] (with K split, both halves go to the partials and the GLU
 // reduce kernel forms h).
-template <int ACT, int GPC, int FMT, class T, bool GLU>
+// XS: AWQ input scaling, x' = RN(x * s_inv[k]) as the activation tile goes to LDS.
+template <int ACT, int GPC, int FMT, class T, bool GLU, bool XS>
 __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   constexpr int kMT = T::kMT, kBM = T::kBM, kWaves = T::kWaves, kThreads = T::kThreads;
   constexpr int kAChunks = T::kAChunks;
@@ -117,6 +119,7 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   struct Regs {
     int kc;
     u4_t a[kAChunks];
+    u4_t xsc;                  // XS: s_inv for this thread's k chunk (the same in every row)
     u4_t b[kPairs][2];         // chunks 16h + c and 32 + 16h + c (h = lane/32, c = lane%16)
     uint32_t s[kPairs][GPC];   // 16-bit scale zero-extended by the load itself
     uint32_t z[kPairs][GPC];
@@ -131,6 +134,9 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
       // a ragged K ends inside the last block: load an in-bounds chunk (zeroed in store_a)
       R.a[i] = *reinterpret_cast<const u4_t*>(p.x + (size_t)gm * K + min(k, K - 8));
     }
+    static_assert(kThreads % 16 == 0, "a thread's k chunk is threadIdx.x % 16 in every row");
+    if constexpr (XS)
+      R.xsc = *reinterpret_cast<const u4_t*>(p.xscale + min(kc * 128 + (int)(threadIdx.x & 15) * 8, K - 8));
     R.kc = kc;
 #pragma unroll
     for (int pr = 0; pr < kPairs; ++pr) {
@@ -155,8 +161,10 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
       const int c = threadIdx.x + kThreads * i;
       const int row = c >> 4, kch = c & 15;
       const bool in_k = R.kc * 128 + kch * 8 < K;
+      u4_t v = R.a[i];
+      if constexpr (XS) v = scale_act8<ACT>(v, R.xsc);
       *reinterpret_cast<u4_t*>(lds_a + buf * kBM * kAStride + row * kAStride + kch * 8) =
-          in_k ? R.a[i] : u4_t{0u, 0u, 0u, 0u};
+          in_k ? v : u4_t{0u, 0u, 0u, 0u};
     }
   };
 
@@ -387,16 +395,28 @@ TiledGeometry tiled_geometry(int M, int K, int N) {
 template <int ACT, int GPC, class T, bool GLU>
 hipError_t launch_glu(const GemmArgs& a, const TiledParams& p, dim3 grid) {
   if (a.nf4)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4, T, GLU, false>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   else if (a.qzeros)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, GLU, false>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   else
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T, GLU, false>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+  return hipGetLastError();
+}
+
+// AWQ-scaled activations: the plain GEMM, affine formats
+template <int ACT, int GPC, class T>
+hipError_t launch_xs(const GemmArgs& a, const TiledParams& p, dim3 grid) {
+  if (a.nf4 || a.glu) return hipErrorNotSupported;
+  if (a.qzeros)
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, false, true>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+  else
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T, false, true>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   return hipGetLastError();
 }
 
 template <int ACT, int GPC, class T>
 hipError_t launch_fmt(const GemmArgs& a, const TiledParams& p, dim3 grid) {
+  if (a.xscale) return launch_xs<ACT, GPC, T>(a, p, grid);
   return a.glu ? launch_glu<ACT, GPC, T, true>(a, p, grid) : launch_glu<ACT, GPC, T, false>(a, p, grid);
 }
 
@@ -451,6 +471,7 @@ hipError_t launch_tiled(const GemmArgs& a) {
   p.kps = g.kps;
   p.partials = g.S > 1 ? static_cast<float*>(a.workspace) : nullptr;
   p.half = p.NT / 2;
+  p.xscale = static_cast<const uint16_t*>(a.xscale);
   const dim3 grid(g.tiles_m * g.tiles_n, g.S);
   const hipError_t e = g.small ? launch_act<SmallTile>(a, p, grid) : launch_act<LargeTile>(a, p, grid);
   if (e != hipSuccess || g.S == 1) return e;

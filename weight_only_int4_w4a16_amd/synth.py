@@ -26,6 +26,7 @@ ROLE_X = 1
 ROLE_CODES = 2
 ROLE_SCALES = 3
 ROLE_ZEROS = 4
+ROLE_XSCALE = 5
 
 COL_BLOCK = 256
 
@@ -83,6 +84,18 @@ def random_scales(rows: int, cols: int, seed: int, dtype: str = "f16",
                   lo: float = 0.004, hi: float = 0.009) -> np.ndarray:
     """Positive scales ~ U(lo, hi): np.float16, or uint16 bf16 bits."""
     s = generator(seed).uniform(lo, hi, size=(rows, cols)).astype(np.float32)
+    if dtype == "f16":
+        return s.astype(np.float16)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(s)
+    raise ValueError(dtype)
+
+
+def channel_scales(K: int, seed: int, dtype: str = "f16", spread: float = 4.0) -> np.ndarray:
+    """Per-input-channel factors for scaled activations: ``2**u`` with u ~ U(-log2 spread,
+    log2 spread), stored as np.float16 or uint16 bf16 bits (a positive ``(K,)`` vector)."""
+    u = generator(seed).uniform(-np.log2(spread), np.log2(spread), size=K)
+    s = np.exp2(u).astype(np.float32)
     if dtype == "f16":
         return s.astype(np.float16)
     if dtype == "bf16":
