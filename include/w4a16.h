@@ -120,9 +120,10 @@ w4a16_status w4a16_gemm_swiglu(const void* x, int M, int K, int N2, w4a16_dtype 
                                size_t workspace_bytes, void* stream);
 
 /* Bytes of scratch device memory w4a16_gemm_awq needs for this shape on the current device:
- * as w4a16_workspace_bytes, except for decode shapes (M <= 16) whose activations do not fit
- * the kernel's LDS staging, which get min(M, 16) * K * 2 bytes (256-byte multiple) for the
- * scaled activations. Returns 0 for bad shapes. */
+ * as w4a16_workspace_bytes, plus room for the scaled activations where they are formed by a
+ * pre-pass: M * K * 2 bytes (256-byte multiples) for decode shapes (M <= 16) whose
+ * activations do not fit the kernel's LDS staging, and for batched shapes on the 128 x 512
+ * tile. Returns 0 for bad shapes. */
 size_t w4a16_awq_workspace_bytes(int M, int K, int N, int group_size);
 
 /* The W4A16 GEMM of AWQ-scaled activations ("4.3 Weight-only INT4", section 3.2: the weight
@@ -130,8 +131,8 @@ size_t w4a16_awq_workspace_bytes(int M, int K, int N, int group_size);
  * with S = diag(s) one factor per input channel):
  *   y = x' @ W_hat,  x'[m][k] = RN_act(x[m][k] * s_inv[k])
  * one round-to-nearest-even of the exact product of two act values, formed as x is staged
- * for the MFMAs (decode shapes whose x does not fit in LDS: by a first small kernel into the
- * workspace).
+ * for the MFMAs (decode shapes whose x does not fit in LDS, and batched shapes on the
+ * 128 x 512 tile: by a first small kernel into the workspace).
  *   s_inv     [in]  act [K], the per-input-channel S^-1, 16-byte aligned
  *   workspace [in/out] >= w4a16_awq_workspace_bytes(M, K, N, group_size) bytes, 256-byte
  *                   aligned (may be NULL when that size is 0)

@@ -109,6 +109,10 @@ def test_awq_rejects_bad_s_inv_and_sizes_its_workspace(L):
     assert awq_workspace_bytes(16, 14336, 4096, 128) == 16 * 14336 * 2
     assert awq_workspace_bytes(9, 9216, 256, 128) == 9 * 9216 * 2
     assert awq_workspace_bytes(200, 2048, 64, 128) == workspace_bytes(200, 2048, 64, 128) > 0
+    assert awq_workspace_bytes(2048, 8192, 28672, 128) == 2048 * 8192 * 2   # 128x512 tile
+    assert awq_workspace_bytes(129, 4224, 28688, 64) == \
+        workspace_bytes(129, 4224, 28688, 64) + 129 * 4224 * 2                 # and K split
+    assert awq_workspace_bytes(513, 2080, 44048, 32) == (513 * 2080 * 2 + 255) // 256 * 256
     assert awq_workspace_bytes(16, 4096, 4104, 128) == 0   # N % 16: no shape
 
 

@@ -2,8 +2,9 @@
 
 "4.3 Weight-only INT4", section 3.2: the deployed weight is the INT4 format of S W and the
 GEMM multiplies the scaled activations, Y_hat = (X S^-1) D(Q(S W)). The library forms
-x' = RN(x * s_inv) as it stages x (decode kernel LDS, batched kernel LDS tile; decode shapes
-whose x does not fit in LDS scale into the workspace first). Checked here:
+x' = RN(x * s_inv) as it stages x (decode kernel LDS, batched kernel's 64x256 LDS tile;
+decode shapes whose x does not fit in LDS, and the 128x512 tile, scale into the workspace
+first). Checked here:
 
 * x' itself, bit for bit, on every path: sparse x and one-hot weight columns make the fp32
   output the scaled activations exactly;
@@ -104,7 +105,8 @@ FULL = [
     (8, 8192, 57344, 128, "bf16", "sym"),   # persistent workgroups
     (16, 14336, 4096, 128, "f16", "asym"),  # x scaled into the workspace
     (256, 4096, 14336, 128, "f16", "asym"),
-    (512, 2080, 44048, 32, "f16", "asym"),
+    (512, 2080, 44048, 32, "f16", "asym"),  # 128x512 tile: x scaled into the workspace
+    (129, 4224, 28688, 64, "bf16", "asym"), # and K split: x' after the partials
     (2048, 8192, 28672, 128, "bf16", "asym"),
 ]
 
@@ -134,6 +136,7 @@ def test_awq_full_size_sampled_strips(M, K, N, g, act, fmt):
     (16, 14336, 512, "f16"),
     (64, 2048, 512, "f16"),      # batched
     (300, 1024, 1024, "bf16"),
+    (1024, 2048, 16384, "bf16"), # batched 128x512 tile: x scaled into the workspace
 ])
 def test_awq_scaled_activations_bit_exact(M, K, N, act):
     """Each row of x holds one nonzero per 128-k block and column n of W_hat is the unit

@@ -36,11 +36,12 @@ size_t workspace_need(int M, int K, int N, int gs) {
   return w4a16::decode_config(M < 16 ? M : 16, K, N, gs, false).workspace_bytes;
 }
 
-// AWQ-scaled x: decode launches whose x does not fit in LDS scale it into the workspace first
+// AWQ-scaled x: decode launches whose x does not fit in LDS, and batched launches on the
+// large tile, scale it into the workspace first
 size_t awq_workspace_need(int M, int K, int N, int gs) {
   GemmArgs a{};
   a.M = M; a.K = K; a.N = N; a.group_size = gs;
-  if (use_tiled(a)) return w4a16::tiled_workspace_bytes(M, K, N);
+  if (use_tiled(a)) return w4a16::tiled_awq_workspace_bytes(M, K, N);
   return w4a16::decode_awq_workspace_bytes(M < 16 ? M : 16, K, N, gs);
 }
 

@@ -129,19 +129,29 @@ DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu) {
 
 namespace {
 
-// AWQ input scaling for launches whose x does not fit in LDS: x' = RN(x * s_inv[k]) written
-// to the workspace, one 16-byte chunk (8 activations) per thread, then the plain kernel.
+// AWQ input scaling as a pre-pass (decode launches whose x does not fit in LDS, batched
+// launches on the large tile): x' = RN(x * s_inv[k]) written to the workspace, one 16-byte
+// chunk (8 activations) per thread; the plain kernel then reads x'.
 template <int ACT>
 __global__ __launch_bounds__(256) void awq_scale_kernel(const u4_t* __restrict__ x,
                                                         const u4_t* __restrict__ s_inv, int K8,
-                                                        int chunks, u4_t* __restrict__ out) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+                                                        size_t chunks, u4_t* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < chunks) out[i] = scale_act8<ACT>(x[i], s_inv[i % K8]);
 }
 
-size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
-
 }  // namespace
+
+hipError_t launch_awq_scale(const void* x, const void* s_inv, int rows, int K, int act, void* out,
+                            hipStream_t stream) {
+  const size_t chunks = (size_t)rows * (K / 8);
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(act == ACT_F16 ? awq_scale_kernel<ACT_F16> : awq_scale_kernel<ACT_BF16>,
+                     dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const u4_t*>(x), static_cast<const u4_t*>(s_inv), K / 8, chunks,
+                     static_cast<u4_t*>(out));
+  return hipGetLastError();
+}
 
 // Rows of x one launch takes: at most 16, one MFMA tile (larger M goes to the batched
 // kernel; a caller of this launcher with more rows gets several launches).
@@ -172,12 +182,7 @@ hipError_t launch_decode(const GemmArgs& a) {
     if (a.xscale && c.x_in_lds) {
       p.xscale = static_cast<const uint16_t*>(a.xscale);
     } else if (a.xscale) {  // x' to the workspace (launches run in order on the stream)
-      const int chunks = rows * (a.K / 8);
-      hipLaunchKernelGGL(a.act == ACT_F16 ? awq_scale_kernel<ACT_F16> : awq_scale_kernel<ACT_BF16>,
-                         dim3(ceil_div(chunks, 256)), dim3(256), 0, a.stream,
-                         reinterpret_cast<const u4_t*>(p.x), static_cast<const u4_t*>(a.xscale),
-                         a.K / 8, chunks, static_cast<u4_t*>(a.workspace));
-      const hipError_t e = hipGetLastError();
+      const hipError_t e = launch_awq_scale(p.x, a.xscale, rows, a.K, a.act, a.workspace, a.stream);
       if (e != hipSuccess) return e;
       p.x = static_cast<const uint16_t*>(a.workspace);
     }

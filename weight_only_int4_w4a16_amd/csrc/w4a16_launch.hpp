@@ -47,6 +47,7 @@ struct DecodeConfig {
 DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu);
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 hipError_t launch_pack(const uint32_t* qweight, int K, int N, uint32_t* packed, hipStream_t s);
 hipError_t launch_dequant(const GemmArgs& a);  // writes W_hat [K][N] into a.out (act dtype)
@@ -54,6 +55,10 @@ hipError_t launch_decode(const GemmArgs& a);   // M <= 16 (more rows: several la
 hipError_t launch_tiled(const GemmArgs& a);    // M > 16
 size_t tiled_workspace_bytes(int M, int K, int N);
 size_t decode_awq_workspace_bytes(int M, int K, int N, int group_size);  // M <= 16
+size_t tiled_awq_workspace_bytes(int M, int K, int N);
+// x'[rows][K] = RN(x * s_inv[k]) (act dtype) into out, 16-byte aligned, K % 8 == 0
+hipError_t launch_awq_scale(const void* x, const void* s_inv, int rows, int K, int act, void* out,
+                            hipStream_t stream);
 const char* decode_name(int M, int K, int N, int group_size, int act);
 const char* tiled_name(int M, int K, int N);
 bool tiled_supported(const GemmArgs& a);

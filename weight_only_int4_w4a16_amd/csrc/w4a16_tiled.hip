@@ -23,6 +23,8 @@
 // contiguous slices, one workgroup each. Every slice stores its fp32 partial tile in the
 // workspace and a second small kernel sums the S partials in slice order (deterministic)
 // into the output.
+#include <type_traits>
+
 #include "w4a16_device.hpp"
 #include "w4a16_launch.hpp"
 
@@ -403,20 +405,26 @@ hipError_t launch_glu(const GemmArgs& a, const TiledParams& p, dim3 grid) {
   return hipGetLastError();
 }
 
-// AWQ-scaled activations: the plain GEMM, affine formats
+// AWQ-scaled activations, small tile: the plain GEMM, affine formats, x scaled as it is
+// staged (the large tile takes x' from a pre-pass instead: the multiply there cost 8% of the
+// bf16 prefill GEMM against 1-2% for the pre-pass)
 template <int ACT, int GPC, class T>
 hipError_t launch_xs(const GemmArgs& a, const TiledParams& p, dim3 grid) {
-  if (a.nf4 || a.glu) return hipErrorNotSupported;
-  if (a.qzeros)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, false, true>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
-  else
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T, false, true>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
-  return hipGetLastError();
+  if constexpr (!std::is_same<T, SmallTile>::value) {
+    return hipErrorNotSupported;
+  } else {
+    if (a.nf4 || a.glu) return hipErrorNotSupported;
+    if (a.qzeros)
+      hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, false, true>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+    else
+      hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T, false, true>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+    return hipGetLastError();
+  }
 }
 
 template <int ACT, int GPC, class T>
 hipError_t launch_fmt(const GemmArgs& a, const TiledParams& p, dim3 grid) {
-  if (a.xscale) return launch_xs<ACT, GPC, T>(a, p, grid);
+  if (p.xscale) return launch_xs<ACT, GPC, T>(a, p, grid);
   return a.glu ? launch_glu<ACT, GPC, T, true>(a, p, grid) : launch_glu<ACT, GPC, T, false>(a, p, grid);
 }
 
@@ -442,6 +450,12 @@ const char* tiled_name(int M, int K, int N) {
   const TiledGeometry g = tiled_geometry(M, K, N);
   if (g.small) return g.S > 1 ? "w4a16_tiled_64x256_splitk" : "w4a16_tiled_64x256";
   return g.S > 1 ? "w4a16_tiled_128x512_splitk" : "w4a16_tiled_128x512";
+}
+
+// AWQ: the large tile reads x' from a pre-pass, placed after the split-K partials
+size_t tiled_awq_workspace_bytes(int M, int K, int N) {
+  const TiledGeometry g = tiled_geometry(M, K, N);
+  return g.small ? g.partial_bytes : align256(g.partial_bytes) + align256((size_t)M * K * 2);
 }
 
 size_t tiled_workspace_bytes(int M, int K, int N) {
@@ -472,6 +486,13 @@ hipError_t launch_tiled(const GemmArgs& a) {
   p.partials = g.S > 1 ? static_cast<float*>(a.workspace) : nullptr;
   p.half = p.NT / 2;
   p.xscale = static_cast<const uint16_t*>(a.xscale);
+  if (a.xscale && !g.small) {
+    void* xs = static_cast<char*>(a.workspace) + align256(g.partial_bytes);
+    const hipError_t e = launch_awq_scale(a.x, a.xscale, a.M, a.K, a.act, xs, a.stream);
+    if (e != hipSuccess) return e;
+    p.x = static_cast<const uint16_t*>(xs);
+    p.xscale = nullptr;
+  }
   const dim3 grid(g.tiles_m * g.tiles_n, g.S);
   const hipError_t e = g.small ? launch_act<SmallTile>(a, p, grid) : launch_act<LargeTile>(a, p, grid);
   if (e != hipSuccess || g.S == 1) return e;
