@@ -21,6 +21,7 @@ Modules
   glu       SwiGLU epilogue of a fused gate+up projection, and its parity bound
   gptq      GPTQ: row-by-row quantization with inverse-Hessian error compensation
   awq       AWQ: per-input-channel scale search, S W quantized, activations times S^-1
+  w4a8      W4A8: per-token INT8 activations, per-channel INT4 weights, integer product
   storage   bytes and bits per weight of the packed format
   roofline  memory/compute floors and the batch crossover
 
@@ -38,6 +39,7 @@ from .gemm import gemm_ref, gemm_ref_columns, gemm_bruteforce
 from .glu import silu, swiglu_split, swiglu_ref, swiglu_bound
 from .gptq import hessian, compensate, gptq_quantize
 from . import awq
+from . import w4a8
 from .storage import storage_bytes, bits_per_weight, bytes_per_weight
 from . import roofline
 
@@ -50,6 +52,6 @@ __all__ = [
     "dequant_affine", "dequant_sym", "dequant_nf4",
     "gemm_ref", "gemm_ref_columns", "gemm_bruteforce",
     "silu", "swiglu_split", "swiglu_ref", "swiglu_bound",
-    "hessian", "compensate", "gptq_quantize", "awq",
+    "hessian", "compensate", "gptq_quantize", "awq", "w4a8",
     "storage_bytes", "bits_per_weight", "bytes_per_weight", "roofline",
 ]

@@ -541,6 +541,86 @@ def test_awq_lowers_the_output_error_against_rtn(sym, dt):
     assert np.sum((y - y0) ** 2) == pytest.approx(min(errs), rel=1e-9)
 
 
+# ---------------------------------------------------------------- W4A8
+
+def test_w4a8_activation_codes_hand_worked():
+    # a row whose largest magnitude is 127 has sx = 1 exactly, so the codes are rint(x):
+    # 63.5 -> 64 and 2.5 -> 2 (ties to even), -0.5 -> -0, 127 -> 127
+    x = np.array([[127.0, 63.5, -0.5, 2.5, -1.25], [0.0, 0.0, 0.0, 0.0, 0.0]], dtype=np.float16)
+    xq, sx = oracle.w4a8.quantize_act_int8(x, "f16")
+    assert sx.dtype == np.float32 and sx.tolist() == [1.0, 0.0]
+    assert xq.tolist() == [[127, 64, 0, 2, -1], [0, 0, 0, 0, 0]]
+    # a negative extreme maps to -127, and the scale is the fp32 quotient max|x| / 127
+    xb = oracle.round_nearest_bf16_bits(np.array([[-3.0, 1.5, 0.75]]))
+    xq, sx = oracle.w4a8.quantize_act_int8(xb, "bf16")
+    assert sx[0] == np.float32(3.0) / np.float32(127.0)
+    assert xq.tolist() == [[-127, 64, 32]]   # 1.5 / (3/127) = 63.5 -> 64; 31.75 -> 32
+
+
+def test_w4a8_activation_error_at_most_half_a_step():
+    x = synth.activations(8, 512, seed=41, dtype="f16")
+    xq, sx = oracle.w4a8.quantize_act_int8(x, "f16")
+    err = np.abs(x.astype(np.float64) - xq.astype(np.float64) * sx.astype(np.float64)[:, None])
+    # half a step, plus the fp32 rounding of the quotient (half an ulp of |x| / sx, times sx)
+    assert np.all(err <= 0.5 * sx[:, None] + 2.0 ** -24 * np.abs(x.astype(np.float64)) * (1 + 1e-9))
+    assert (err / sx[:, None]).max() > 0.45
+    assert np.all(np.abs(xq).max(axis=1) == 127)
+
+
+def test_w4a8_integer_product_is_exact_bruteforce():
+    rng = np.random.default_rng(42)
+    M, K, N = 3, 16, 8
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    q = rng.integers(-8, 8, (K, N)).astype(np.int8)
+    got = oracle.w4a8.int_gemm(xq, q)
+    for m in range(M):
+        for n in range(N):
+            assert got[m, n] == sum(int(xq[m, k]) * int(q[k, n]) for k in range(K))
+    # the extreme: every term 127 * -8 (or -127 * -8) over a long K stays exact
+    big = oracle.w4a8.int_gemm(np.full((1, 4096), -127, np.int8), np.full((4096, 1), -8, np.int8))
+    assert big[0, 0] == 4096 * 1016
+
+
+def test_w4a8_signed_codes_from_offset_binary():
+    u = np.arange(16, dtype=np.uint8).reshape(16, 1)
+    q = oracle.w4a8.signed_codes(oracle.pack_codes(np.vstack([u, u])))
+    assert q[:16, 0].tolist() == list(range(-8, 8))
+
+
+def test_w4a8_reduces_to_w4a16_when_x_is_on_the_int8_grid():
+    # x = sx * xq exactly (integers with max 127, sx = 1) and power-of-two weight scales:
+    # the W4A8 result equals the W4A16 oracle on the per-channel-scaled weight
+    rng = np.random.default_rng(43)
+    K, N = 64, 16
+    x = rng.integers(-127, 128, (4, K)).astype(np.float16)
+    x[:, 0] = 127
+    W = rng.normal(0, 0.05, (K, N))
+    q, s = oracle.quantize_rtn_sym(W, K, "f16")
+    s = np.float16(2.0) ** np.rint(np.log2(s.astype(np.float64))).astype(np.float16)
+    qw = oracle.pack_codes(oracle.to_offset_binary(q))
+    y8 = oracle.w4a8.gemm_w4a8_ref(x, qw, s, "f16")
+    y16 = oracle.gemm_ref(x, oracle.dequant_sym(qw, s, K))
+    assert np.array_equal(y8, y16)
+
+
+def test_w4a8_error_within_the_activation_quantization_bound():
+    # |y_w4a8 - x W_hat| <= sum_k |x - sx xq| |W_hat| <= sx / 2 * sum_k |W_hat[k, n]|
+    x = synth.activations(6, 256, seed=44, dtype="bf16")
+    W = synth.gaussian_weight(256, 32, seed=45)
+    q, s = oracle.quantize_rtn_sym(W, 256, "bf16")
+    qw = oracle.pack_codes(oracle.to_offset_binary(q))
+    w_hat = oracle.bf16_bits_to_f64(oracle.dequant_sym(qw, s, 256, "bf16"))
+    y8 = oracle.w4a8.gemm_w4a8_ref(x, qw, s, "bf16")
+    y16 = oracle.bf16_bits_to_f64(x) @ w_hat
+    _, sx = oracle.w4a8.quantize_act_int8(x, "bf16")
+    bound = 0.5 * sx.astype(np.float64)[:, None] * np.abs(w_hat).sum(axis=0)[None, :]
+    # the integer result times the stored scales is W_hat's own product up to the one rounding
+    # of each W_hat entry to bf16 (relative 2**-9)
+    slack = 2.0 ** -8 * np.abs(oracle.bf16_bits_to_f64(x)) @ np.abs(w_hat)
+    assert np.all(np.abs(y8 - y16) <= bound + slack)
+    assert np.max(np.abs(y8 - y16) / bound) > 0.02
+
+
 # ---------------------------------------------------------------- NF4
 
 def test_inverse_normal_matches_library():
