@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 METRIC = "W4A16 GEMM effective HBM GB/s at M=1 (% of peak) and TFLOPS at M=256"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+MFMA_I8_PEAK_TOPS = 5033.2     # dense int8 MFMA: twice the fp16 rate (published 5.0 POP/s)
 
 WORKLOADS = {
     # name: shapes (K, N), layers, group size, symmetric, activation dtype, seed config
@@ -360,6 +361,51 @@ def awq(args, torch, w4) -> int:
     return 0
 
 
+def w4a8(args, torch, w4) -> int:
+    """W4A8 (per-token INT8 activations, INT8 MFMA) against W4A16 on the same symmetric codes
+    (the W4A16 call gets the per-channel scale repeated in every group of 128): the crossover
+    shape over M and the prefill shape. Times include W4A8's activation quantization kernel.
+    One JSON line per shape and M."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261206)
+    g = 128
+    cases = [(M, 4096, 14336, torch.float16, 8) for M in (16, 64, 256, 1024, 4096)]
+    cases += [(2048, 8192, 28672, torch.bfloat16, 4)]
+    for (M, K, N, dt, copies) in cases:
+        wts = []
+        for _ in range(copies):
+            qw = torch.randint(-2**31, 2**31 - 1, (K // 8, N), dtype=torch.int32, device=dev,
+                               generator=gen)
+            sw = (torch.rand(N, device=dev, generator=gen) * 0.005 + 0.004).to(dt)
+            wts.append((w4.pack(qw), sw, sw.repeat(K // g, 1).contiguous()))
+        x = torch.randn((M, K), device=dev, generator=gen).to(dt)
+        y = torch.empty((M, N), device=dev, dtype=dt)
+        ws = torch.empty(max(w4.w4a8_workspace_bytes(M, K, N), w4.workspace_bytes(M, K, N, g), 256),
+                         dtype=torch.uint8, device=dev)
+
+        def run16():
+            for (pk, _, sg) in wts:
+                w4.gemm(x, pk, sg, None, g, out=y, workspace=ws)
+
+        def run8():
+            for (pk, sw, _) in wts:
+                w4.gemm_w4a8(x, pk, sw, out=y, workspace=ws)
+
+        res = {k: round(_graph_us(torch, fn, args.steps) / copies, 2)
+               for k, fn in (("w4a16_us", run16), ("w4a8_us", run8))}
+        flops = 2.0 * M * K * N
+        res["w4a16_tflops"] = round(flops / res["w4a16_us"] / 1e6, 1)
+        res["w4a8_tops"] = round(flops / res["w4a8_us"] / 1e6, 1)
+        res["w4a8_frac_of_int8_peak"] = round(res["w4a8_tops"] / MFMA_I8_PEAK_TOPS, 3)
+        res["speedup"] = round(res["w4a16_us"] / res["w4a8_us"], 3)
+        print(json.dumps({"config": "w4a8", "M": M, "K": K, "N": N, "dtype": str(dt).split(".")[-1],
+                          "w4a16_kernel": w4.kernel_name(M, K, N, g), **res}), flush=True)
+        del wts
+        torch.cuda.empty_cache()
+    return 0
+
+
 def mlp(args, torch, w4) -> int:
     """The Llama-3-8B-shaped decode MLP per layer (32 layers of distinct weights, asymmetric
     g128, fp16), replayed from a HIP graph: the fused path is w4a16_gemm_swiglu on the
@@ -423,6 +469,8 @@ def main() -> int:
                     help="time the fused SwiGLU decode MLP against the unfused path, per layer")
     ap.add_argument("--awq", action="store_true",
                     help="time the AWQ-scaled GEMM against the plain GEMM on the same weights")
+    ap.add_argument("--w4a8", action="store_true",
+                    help="time W4A8 (per-token INT8 activations) against W4A16 on the same codes")
     ap.add_argument("--sweep", action="store_true",
                     help="per-(config, shape, M) timing table of every benchmark config, one JSON "
                          "line per row, instead of the step benchmark")
@@ -455,6 +503,8 @@ def main() -> int:
         return mlp(args, torch, w4)
     if args.awq:
         return awq(args, torch, w4)
+    if args.w4a8:
+        return w4a8(args, torch, w4)
     if args.sweep:
         return sweep(args, torch, w4)
 

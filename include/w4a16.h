@@ -144,6 +144,35 @@ w4a16_status w4a16_gemm_awq(const void* x, const void* s_inv, int M, int K, int 
                             w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* Bytes of scratch device memory w4a16_gemm_w4a8 needs: the INT8 activations (M * K), their
+ * scales and code sums (M * 4 each), each part 256-byte aligned. 0 for M = 0 or bad shapes. */
+size_t w4a16_w4a8_workspace_bytes(int M, int K, int N);
+
+/* W4A8: INT4 weights with per-token INT8 activations on the integer MFMA ("INT4 LLMs: What
+ * 4-Bit Quantization Means…", weight-only section: [-8, 7] weights unpacked to INT8, an
+ * INT8 x INT8 product, the result dequantized with the input and per-channel scales; "INT8 vs
+ * INT4 Quantization, in depth", section "Two regimes": past the crossover only the math rate
+ * counts).
+ *   y[m][n] = sx[m] * sw[n] * sum_k xq[m][k] * (u[k][n] - 8)
+ *   sx[m] = RN_f32(max_k |x[m][k]| / 127),  xq = clip(rint(RN_f32(x / sx)), -127, 127)
+ * The integer sum is exact; the epilogue multiplies it by the two scales in fp32.
+ *   x         [in]  act [M][K] (quantized per row by a first kernel into the workspace)
+ *   packed    [in]  output of w4a16_pack of symmetric codes (u = q + 8, as for w4a16_gemm with
+ *                   qzeros = NULL)
+ *   wscale    [in]  act [N], one scale per output channel
+ *   out       [out] out_dtype [M][N], out_dtype = act or W4A16_F32
+ *   workspace [in/out] >= w4a16_w4a8_workspace_bytes(M, K, N), 256-byte aligned
+ * K % 32 == 0 (else W4A16_ERR_UNSUPPORTED); other arguments and errors as for w4a16_gemm. */
+w4a16_status w4a16_gemm_w4a8(const void* x, int M, int K, int N, w4a16_dtype act,
+                             const int32_t* packed, const void* wscale, void* out,
+                             w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Test hook: the per-token INT8 quantization w4a16_gemm_w4a8 applies, in k order.
+ *   xq [out] int8 [M][K] (8-byte aligned), sx [out] float [M]. K % 8 == 0. */
+w4a16_status w4a16_quantize_act_int8(const void* x, int M, int K, w4a16_dtype act, int8_t* xq,
+                                     float* sx, void* stream);
+
 /* NF4 counterpart of w4a16_gemm_swiglu (absmax [K/block_size][N2] fp16, codebook as for
  * w4a16_gemm_nf4). */
 w4a16_status w4a16_gemm_nf4_swiglu(const void* x, int M, int K, int N2, w4a16_dtype act,

@@ -59,8 +59,14 @@ def signed_codes(qweight: np.ndarray) -> np.ndarray:
 
 
 def int_gemm(xq: np.ndarray, q: np.ndarray) -> np.ndarray:
-    """The exact integer product ``xq[M, K] @ q[K, N]`` (int64)."""
-    return np.asarray(xq, dtype=np.int64) @ np.asarray(q, dtype=np.int64)
+    """The exact integer product ``xq[M, K] @ q[K, N]`` (int64). Every term is an integer of
+    magnitude at most 127 * 8, so every partial sum, in any order, is an integer below 2**53
+    (for K < 2**43) and the fp64 matrix product is exact."""
+    K = np.shape(xq)[1]
+    if K * 127 * 8 >= 2 ** 53:
+        raise ValueError("K too large for an exact fp64 product")
+    p = np.asarray(xq, dtype=np.float64) @ np.asarray(q, dtype=np.float64)
+    return p.astype(np.int64)
 
 
 def gemm_w4a8_ref(x: np.ndarray, qweight: np.ndarray, wscale: np.ndarray,
@@ -69,6 +75,6 @@ def gemm_w4a8_ref(x: np.ndarray, qweight: np.ndarray, wscale: np.ndarray,
     ``qweight[K/8, N]`` (offset-binary), one scale per output channel ``wscale[N]`` (or
     ``[1, N]``) stored in ``dtype``."""
     xq, sx = quantize_act_int8(x, dtype)
-    acc = int_gemm(xq, signed_codes(qweight)).astype(np.float64)   # exact below 2**53
+    acc = int_gemm(xq, signed_codes(qweight)).astype(np.float64)   # exact: below 2**53
     sw = _values(np.asarray(wscale).reshape(-1), dtype)
     return acc * sx.astype(np.float64)[:, None] * sw[None, :]

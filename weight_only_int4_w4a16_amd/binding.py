@@ -50,6 +50,12 @@ def lib() -> ctypes.CDLL:
     L.w4a16_awq_workspace_bytes.restype = sz
     L.w4a16_gemm_awq.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
     L.w4a16_gemm_awq.restype = i32
+    L.w4a16_w4a8_workspace_bytes.argtypes = [i32, i32, i32]
+    L.w4a16_w4a8_workspace_bytes.restype = sz
+    L.w4a16_gemm_w4a8.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
+    L.w4a16_gemm_w4a8.restype = i32
+    L.w4a16_quantize_act_int8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    L.w4a16_quantize_act_int8.restype = i32
     L.w4a16_gemm_swiglu.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
     L.w4a16_gemm_swiglu.restype = i32
     L.w4a16_gemm_nf4_swiglu.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
@@ -213,6 +219,41 @@ def gemm_awq(x, s_inv, packed, scales, qzeros, group_size: int, out_dtype=None, 
                               _stream(x))
     _check(st, "w4a16_gemm_awq")
     return out
+
+
+def w4a8_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(lib().w4a16_w4a8_workspace_bytes(M, K, N))
+
+
+def gemm_w4a8(x, packed, wscale, out_dtype=None, out=None, workspace=None):
+    """W4A8: ``y = sx * sw * (xq @ q)`` with x quantized per token to INT8 inside the call,
+    symmetric INT4 codes (packed as for :func:`gemm` with ``qzeros=None``) and one scale per
+    output channel ``wscale[N]`` in x's dtype."""
+    torch = _torch()
+    M, K = x.shape
+    N = wscale.shape[-1]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if wscale.dtype != x.dtype or wscale.numel() != N or not wscale.is_contiguous():
+        raise W4A16Error("wscale must be a contiguous (N,) tensor of the activation dtype")
+    ws = _workspace(x.device, w4a8_workspace_bytes(M, K, N) if M else 0, workspace)
+    st = lib().w4a16_gemm_w4a8(_ptr(x), M, K, N, _dt(x.dtype), _ptr(packed), _ptr(wscale),
+                               _ptr(out), _dt(out.dtype), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream(x))
+    _check(st, "w4a16_gemm_w4a8")
+    return out
+
+
+def quantize_act_int8(x):
+    """The per-token INT8 quantization of the W4A8 path: ``(xq[M, K] int8, sx[M] float32)``."""
+    torch = _torch()
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    st = lib().w4a16_quantize_act_int8(_ptr(x), M, K, _dt(x.dtype), _ptr(xq), _ptr(sx), _stream(x))
+    _check(st, "w4a16_quantize_act_int8")
+    return xq, sx
 
 
 def gemm_swiglu(x, packed, scales, qzeros, group_size: int, out_dtype=None, out=None,

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libw4a16.so")
-SOURCES = ["w4a16_api.hip", "w4a16_pack.hip", "w4a16_decode.hip", "w4a16_tiled.hip"] + [
+SOURCES = ["w4a16_api.hip", "w4a16_pack.hip", "w4a16_decode.hip", "w4a16_tiled.hip",
+           "w4a16_w4a8.hip"] + [
     f"w4a16_decode_{a}_{f}.hip" for a in ("f16", "bf16") for f in ("asym", "sym", "nf4")]
 ARCH = os.environ.get("W4A16_ARCH", "gfx950")
 

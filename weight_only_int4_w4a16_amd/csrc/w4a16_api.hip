@@ -137,6 +137,46 @@ w4a16_status w4a16_gemm_awq(const void* x, const void* s_inv, int M, int K, int 
   return gemm_common(a, act, out_dtype);
 }
 
+size_t w4a16_w4a8_workspace_bytes(int M, int K, int N) {
+  if (M <= 0 || K <= 0 || N <= 0 || K % 32 || N % 16 || (long long)K * N >= (1LL << 34)) return 0;
+  return w4a16::w4a8_workspace_bytes(M, K);
+}
+
+w4a16_status w4a16_gemm_w4a8(const void* x, int M, int K, int N, w4a16_dtype act,
+                             const int32_t* packed, const void* wscale, void* out,
+                             w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (M < 0 || K <= 0 || N <= 0 || K % 8 || N % 8) return W4A16_ERR_ARG;
+  if (K % 32 || N % 16 || (long long)K * N >= (1LL << 34)) return W4A16_ERR_UNSUPPORTED;
+  if (act != W4A16_F16 && act != W4A16_BF16) return W4A16_ERR_ARG;
+  if (out_dtype != act && out_dtype != W4A16_F32) return W4A16_ERR_ARG;
+  if (M == 0) return W4A16_OK;
+  if (!x || !packed || !wscale || !out) return W4A16_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(out, 16) || !aligned(wscale, 2))
+    return W4A16_ERR_ARG;
+  const size_t need = w4a16::w4a8_workspace_bytes(M, K);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+  GemmArgs a{};
+  a.x = x; a.M = M; a.K = K; a.N = N;
+  a.act = act == W4A16_F16 ? w4a16::ACT_F16 : w4a16::ACT_BF16;
+  a.packed = reinterpret_cast<const uint32_t*>(packed);
+  a.scales = wscale;
+  a.out = out; a.out_dtype = (int)out_dtype;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.stream = static_cast<hipStream_t>(stream);
+  return from_hip(w4a16::launch_w4a8(a));
+}
+
+w4a16_status w4a16_quantize_act_int8(const void* x, int M, int K, w4a16_dtype act, int8_t* xq,
+                                     float* sx, void* stream) {
+  if (M < 0 || K <= 0 || K % 8) return W4A16_ERR_ARG;
+  if (act != W4A16_F16 && act != W4A16_BF16) return W4A16_ERR_ARG;
+  if (M == 0) return W4A16_OK;
+  if (!x || !xq || !sx || !aligned(x, 16) || !aligned(xq, 8) || !aligned(sx, 4)) return W4A16_ERR_ARG;
+  return from_hip(w4a16::launch_quantize_act(x, M, K, act == W4A16_F16 ? w4a16::ACT_F16 : w4a16::ACT_BF16,
+                                             false, xq, sx, nullptr, static_cast<hipStream_t>(stream)));
+}
+
 w4a16_status w4a16_gemm_swiglu(const void* x, int M, int K, int N2, w4a16_dtype act,
                                const int32_t* packed, const void* scales, const int32_t* qzeros,
                                int group_size, void* out, w4a16_dtype out_dtype, void* workspace,
