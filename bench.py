@@ -296,24 +296,27 @@ def sweep(args, torch, w4) -> int:
     return 0
 
 
-def _graph_us(torch, fn, steps: int) -> float:
-    """us per replay of a HIP graph capturing fn (3 warm-up replays, then steps timed)."""
+def _graph_us(torch, fn, steps: int, graph: bool = True) -> float:
+    """us per replay of a HIP graph capturing fn (3 warm-up replays, then steps timed); with
+    graph=False, fn's launches run eagerly (for counter collection)."""
     fn()
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        fn()
+    run = fn
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        run = g.replay
     for _ in range(3):
-        graph.replay()
+        run()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        graph.replay()
+        run()
     e1.record()
     torch.cuda.synchronize()
-    del graph
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
@@ -372,6 +375,8 @@ def w4a8(args, torch, w4) -> int:
     g = 128
     cases = [(M, 4096, 14336, torch.float16, 8) for M in (16, 64, 256, 1024, 4096)]
     cases += [(2048, 8192, 28672, torch.bfloat16, 4)]
+    if args.m is not None:
+        cases = [c for c in cases if c[0] == args.m]
     for (M, K, N, dt, copies) in cases:
         wts = []
         for _ in range(copies):
@@ -392,8 +397,19 @@ def w4a8(args, torch, w4) -> int:
             for (pk, sw, _) in wts:
                 w4.gemm_w4a8(x, pk, sw, out=y, workspace=ws)
 
-        res = {k: round(_graph_us(torch, fn, args.steps) / copies, 2)
+        res = {k: round(_graph_us(torch, fn, args.steps, not args.no_graph) / copies, 2)
                for k, fn in (("w4a16_us", run16), ("w4a8_us", run8))}
+        # comparator: a dense INT8 x INT8 -> INT32 GEMM of the same shape (torch._int_mm,
+        # hipBLASLt), activations already quantized and the weight 8-bit (twice the bytes)
+        try:
+            a8 = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=gen)
+            b8 = torch.randint(-8, 8, (N, K), dtype=torch.int8, device=dev, generator=gen).t()
+            res["dense_int8_us"] = round(_graph_us(torch, lambda: torch._int_mm(a8, b8), args.steps,
+                                                   not args.no_graph), 2)
+            del a8, b8
+        except Exception as e:  # noqa: BLE001 - a comparator only
+            res["dense_int8_us"] = None
+            res["dense_int8_error"] = str(e)[:120]
         flops = 2.0 * M * K * N
         res["w4a16_tflops"] = round(flops / res["w4a16_us"] / 1e6, 1)
         res["w4a8_tops"] = round(flops / res["w4a8_us"] / 1e6, 1)

@@ -37,19 +37,22 @@ typedef int i4v_t __attribute__((ext_vector_type(4)));
 typedef int i16v_t __attribute__((ext_vector_type(16)));
 
 constexpr int kQThreads = 256;      // quantizer workgroup
-constexpr int kARow = 128 + 16;     // LDS row stride of the xq tile (bytes)
 
-template <int MT, int WAVES>
+// MT 32-row MFMA tiles by WAVES waves of 64 columns; each pipeline stage (one LDS buffer and
+// one register set) covers KB k-blocks of 128.
+template <int MT, int WAVES, int KB>
 struct I8Tile {
   static constexpr int kMT = MT;
   static constexpr int kBM = 32 * MT;
   static constexpr int kWaves = WAVES;
   static constexpr int kThreads = 64 * WAVES;
-  static constexpr int kAChunks = kBM * 8 / kThreads;  // 16-byte xq chunks per thread per block
+  static constexpr int kKB = KB;
+  static constexpr int kARow = 128 * KB + 16;           // LDS row stride of the xq tile (bytes)
+  static constexpr int kAChunks = kBM * 8 * KB / kThreads;  // 16-byte xq chunks per thread
   static constexpr size_t kLdsBytes = 2 * kBM * kARow;
 };
-typedef I8Tile<4, 8> I8Large;
-typedef I8Tile<2, 4> I8Small;
+typedef I8Tile<4, 8, 1> I8Large;
+typedef I8Tile<2, 4, 1> I8Small;
 
 template <int ACT>
 __device__ inline float act_value(uint16_t b) {
@@ -148,7 +151,8 @@ struct W4A8Params {
 template <class T>
 __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
   constexpr int kMT = T::kMT, kBM = T::kBM, kWaves = T::kWaves, kThreads = T::kThreads;
-  constexpr int kAChunks = T::kAChunks;
+  constexpr int kAChunks = T::kAChunks, kKB = T::kKB, kARow = T::kARow;
+  constexpr int kCPR = 8 * kKB;  // 16-byte chunks per tile row per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_q[];  // [2][kBM * kARow]
 
   const int lane = threadIdx.x & 63;
@@ -160,35 +164,41 @@ __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
   const int nt0 = tn * (kWaves * 4) + wave * 4;  // this wave's first strip
   const int h = lane >> 5;
 
+  // a stage: the xq chunks this thread copies to LDS and, per k-block, the codes of this
+  // wave's strips. Blocks past K (a last stage short of KB blocks) reload the last block's
+  // codes; their activations are zero, so they add nothing.
   struct Regs {
     int kc;
     u4_t a[kAChunks];
-    u4_t b[2][2];  // pair, chunk 32h + l%16 / 32h + 16 + l%16
+    u4_t b[kKB][2][2];  // block, pair, chunk 32h + l%16 / 32h + 16 + l%16
   };
   auto load = [&](Regs& R, int kc) {
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
       const int c = threadIdx.x + kThreads * i;
-      const int row = c >> 3, kch = c & 7;
+      const int row = c / kCPR, kch = c % kCPR;
       const int gm = min(m0 + row, M - 1);
       const int k = kc * 128 + kch * 16;
-      // a ragged K ends inside the last block: an in-bounds chunk, zeroed in store_a
+      // past K (a ragged last block, or a stage's missing blocks): an in-bounds chunk, zeroed
+      // in store_a
       R.a[i] = *reinterpret_cast<const u4_t*>(p.xq + (size_t)gm * K + min(k, K - 16));
     }
     R.kc = kc;
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      const int nt = min(nt0 + 2 * pr + ((lane >> 4) & 1), p.NT - 1);  // past N: never stored
-      const u4_t* blk = p.packed + ((size_t)nt * KC + kc) * 64 + 32 * h + (lane & 15);
-      R.b[pr][0] = __builtin_nontemporal_load(blk);
-      R.b[pr][1] = __builtin_nontemporal_load(blk + 16);
-    }
+    for (int d = 0; d < kKB; ++d)
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int nt = min(nt0 + 2 * pr + ((lane >> 4) & 1), p.NT - 1);  // past N: never stored
+        const u4_t* blk = p.packed + ((size_t)nt * KC + min(kc + d, KC - 1)) * 64 + 32 * h + (lane & 15);
+        R.b[d][pr][0] = __builtin_nontemporal_load(blk);
+        R.b[d][pr][1] = __builtin_nontemporal_load(blk + 16);
+      }
   };
   auto store_a = [&](const Regs& R, int buf) {
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
       const int c = threadIdx.x + kThreads * i;
-      const int row = c >> 3, kch = c & 7;
+      const int row = c / kCPR, kch = c % kCPR;
       const bool in_k = R.kc * 128 + kch * 16 < K;
       *reinterpret_cast<u4_t*>(lds_q + buf * kBM * kARow + row * kARow + kch * 16) =
           in_k ? R.a[i] : u4_t{0u, 0u, 0u, 0u};
@@ -203,41 +213,49 @@ __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][pr][i] = 0;
 
+  // The A fragments of step s + 1 are read from LDS while step s's MFMAs run (two sets of
+  // kMT fragments), so an MFMA never waits on the LDS read right before it.
   auto compute = [&](const Regs& R, int buf) {
-    const uint8_t* as = lds_q + buf * kBM * kARow;
+    const uint8_t* as = lds_q + buf * kBM * kARow + (lane & 31) * kARow + h * 16;
+    i4v_t af[2][kMT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // 32-k steps of the block
+    for (int mt = 0; mt < kMT; ++mt) af[0][mt] = *reinterpret_cast<const i4v_t*>(as + mt * 32 * kARow);
+#pragma unroll
+    for (int s = 0; s < 4 * kKB; ++s) {  // 32-k steps of the stage
+      if (s + 1 < 4 * kKB) {
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt)
+          af[(s + 1) & 1][mt] = *reinterpret_cast<const i4v_t*>(as + mt * 32 * kARow + (s + 1) * 32);
+      }
       i4v_t bq[2];
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
-        const uint32_t w0 = R.b[pr][0][s], w1 = R.b[pr][1][s];
+        const uint32_t w0 = R.b[s >> 2][pr][0][s & 3], w1 = R.b[s >> 2][pr][1][s & 3];
         bq[pr] = i4v_t{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
                        (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
       }
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        const i4v_t a = *reinterpret_cast<const i4v_t*>(as + (mt * 32 + (lane & 31)) * kARow + s * 32 + h * 16);
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr)
-          acc[mt][pr] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq[pr], acc[mt][pr], 0, 0, 0);
-      }
+          acc[mt][pr] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][mt], bq[pr], acc[mt][pr], 0, 0, 0);
     }
   };
 
-  // two register sets and two LDS buffers: block i+1 loads while block i is multiplied
-  const int nb = KC;
+  // two register sets and two LDS buffers: stage i+1 loads while stage i is multiplied
+  const int nb = (KC + kKB - 1) / kKB;
   Regs R0, R1;
   load(R0, 0);
   store_a(R0, 0);
   __syncthreads();
   int i = 0;
   for (; i + 1 < nb; i += 2) {
-    load(R1, i + 1);
+    load(R1, (i + 1) * kKB);
     __builtin_amdgcn_sched_barrier(0);
     compute(R0, 0);
     store_a(R1, 1);
     __syncthreads();
-    load(R0, min(i + 2, nb - 1));
+    load(R0, min(i + 2, nb - 1) * kKB);
     __builtin_amdgcn_sched_barrier(0);
     compute(R1, 1);
     store_a(R0, 0);
