@@ -142,3 +142,32 @@ def oracle_columns(x, qweight, scales, qzeros, g, act, cols, nf4=False, codebook
             qz = oracle.pack_zeros(zfull[:, idx])
         w_hat = oracle.dequant_affine(qw, s, qz, g, act)
     return oracle.gemm_ref(x, w_hat, act)
+
+
+def assert_graph_replays_match_eager(step, outs, replays: int = 4):
+    """Run ``step`` (launches writing ``outs``) eagerly, capture it in a HIP graph, and check
+    that every replay, with eager work and synchronisation between replays, reproduces the
+    eager outputs bit for bit."""
+    torch = torch_mod()
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(replays):
+        for o in outs:
+            o.fill_(0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o.view(torch.int16) if o.element_size() == 2 else o.view(torch.int32),
+                               e.view(torch.int16) if e.element_size() == 2 else e.view(torch.int32)), \
+                f"replay {r}, output {i}"

@@ -20,8 +20,8 @@ import pytest
 import oracle
 from weight_only_int4_w4a16_amd import synth
 
-from gpu_common import (assert_close, from_dev, oracle_columns, require_gpu, sample_strips,
-                        to_dev, torch_mod)
+from gpu_common import (assert_close, assert_graph_replays_match_eager, from_dev, oracle_columns,
+                        require_gpu, sample_strips, to_dev, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -203,3 +203,28 @@ def test_awq_search_end_to_end(M, act, sym):
         errs_gpu.append(np.linalg.norm(y - xv @ W))
     assert errs_gpu[0] < errs_gpu[1], f"AWQ {errs_gpu[0]:.4g} not below RTN {errs_gpu[1]:.4g}"
 
+
+
+def test_awq_graph_replays_match_eager():
+    """Every AWQ path captured in one HIP graph (LDS prologue, persistent, workspace pre-pass
+    for decode and for the 128x512 tile, split K): replays equal the eager run bit for bit."""
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    shapes = [(1, 1024, 512), (16, 2048, 28672), (12, 14336, 256), (130, 2048, 64), (1024, 2048, 16384)]
+    calls, outs = [], []
+    for i, (M, K, N) in enumerate(shapes):
+        _announce(f"awq graph M={M} K={K} N={N} {_path(M, K, N, 128)}")
+        qw, sc, qz = synth.timing_weights(K, N, 128, 70 + i, scale_dtype="f16")
+        x = to_dev(synth.activations(M, K, 80 + i, "f16"), "f16")
+        s_inv = to_dev(synth.channel_scales(K, 90 + i, "f16"), "f16")
+        args = (x, s_inv, w4.pack(to_dev(qw, "i32")), to_dev(sc, "f16"), to_dev(qz, "i32"), 128)
+        ws = torch.empty(max(w4.awq_workspace_bytes(M, K, N, 128), 256), dtype=torch.uint8, device="cuda")
+        out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        calls.append((args, ws, out))
+        outs.append(out)
+
+    def step():
+        for args, ws, out in calls:
+            w4.gemm_awq(*args, out=out, workspace=ws)
+
+    assert_graph_replays_match_eager(step, outs)

@@ -17,7 +17,8 @@ import pytest
 import oracle
 from weight_only_int4_w4a16_amd import synth
 
-from gpu_common import from_dev, require_gpu, sample_strips, to_dev, torch_mod
+from gpu_common import (assert_graph_replays_match_eager, from_dev, require_gpu, sample_strips,
+                        to_dev, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -137,3 +138,26 @@ def test_w4a8_against_w4a16_within_activation_bound(M, act):
     bound = 0.5 * sx.astype(np.float64)[:, None] * np.abs(wv).sum(axis=0)[None, :]
     slack = 2.0 ** -7 * np.abs(xv) @ np.abs(wv) + 1e-3 * np.abs(y16).max()
     assert np.all(np.abs(y8 - y16) <= bound + slack)
+
+
+def test_w4a8_graph_replays_match_eager():
+    """The quantizer and both GEMM tiles captured in one HIP graph: replays equal the eager run
+    bit for bit."""
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    calls, outs = [], []
+    for i, (M, K, N, act) in enumerate([(64, 2048, 1024, "f16"), (600, 1024, 16384, "bf16")]):
+        _announce(f"w4a8 graph M={M} K={K} N={N} {act}")
+        qw, _, _ = synth.timing_weights(K, N, 128, 100 + i, symmetric=True, scale_dtype=act)
+        sw = synth.random_scales(1, N, 110 + i, act).reshape(-1)
+        x = to_dev(_x(M, K, act, 120 + i), act)
+        ws = torch.empty(w4.w4a8_workspace_bytes(M, K, N), dtype=torch.uint8, device="cuda")
+        out = torch.empty((M, N), dtype=x.dtype, device="cuda")
+        calls.append(((x, w4.pack(to_dev(qw, "i32")), to_dev(sw, act)), ws, out))
+        outs.append(out)
+
+    def step():
+        for args, ws, out in calls:
+            w4.gemm_w4a8(*args, out=out, workspace=ws)
+
+    assert_graph_replays_match_eager(step, outs)

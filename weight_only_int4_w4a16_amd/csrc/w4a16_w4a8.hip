@@ -263,25 +263,34 @@ __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
   }
   if (i < nb) compute(R0, 0);
 
-  // ---- epilogue: lane l holds column 32 pair + l%32, rows 32 mt + 8 (i/4) + 4 (l/32) + i%4 ----
+  // ---- epilogue: lane l holds column 32 pair + l%32, rows 32 mt + 8 (i/4) + 4 (l/32) + i%4;
+  // each row's scale and code sum are read once for both pairs ----
+  float sw[2];
+  int col[2];
+  bool in_n[2];
 #pragma unroll
   for (int pr = 0; pr < 2; ++pr) {
     const int nt = nt0 + 2 * pr + ((lane >> 4) & 1);
-    if (nt < p.NT) {
-      const int col = nt * 16 + (lane & 15);
-      const float sw = p.act == ACT_F16 ? act_value<ACT_F16>(p.wscale[col]) : act_value<ACT_BF16>(p.wscale[col]);
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + mt * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (m < M) {
-            const int v = acc[mt][pr][e] - 8 * p.xsum[m];  // exact: sum of xq * (u - 8)
-            store_out(p.out, (size_t)m * p.N + col, (float)v * p.sx[m] * sw, p.out_dtype);
-          }
-        }
-    }
+    in_n[pr] = nt < p.NT;
+    col[pr] = min(nt, p.NT - 1) * 16 + (lane & 15);
+    sw[pr] = p.act == ACT_F16 ? act_value<ACT_F16>(p.wscale[col[pr]]) : act_value<ACT_BF16>(p.wscale[col[pr]]);
   }
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + mt * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (m < M) {
+        const int zs = 8 * p.xsum[m];
+        const float sxm = p.sx[m];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr)
+          if (in_n[pr]) {
+            const int v = acc[mt][pr][e] - zs;  // exact: sum of xq * (u - 8)
+            store_out(p.out, (size_t)m * p.N + col[pr], (float)v * sxm * sw[pr], p.out_dtype);
+          }
+      }
+    }
 }
 
 int cu_count_w4a8() {
