@@ -144,9 +144,15 @@ w4a16_status w4a16_gemm_awq(const void* x, const void* s_inv, int M, int K, int 
                             w4a16_dtype out_dtype, void* workspace, size_t workspace_bytes,
                             void* stream);
 
-/* Bytes of scratch device memory w4a16_gemm_w4a8 needs: the INT8 activations (M * K), their
- * scales and code sums (M * 4 each), each part 256-byte aligned. 0 for M = 0 or bad shapes. */
+/* Bytes of scratch device memory w4a16_gemm_w4a8 needs on the current device: the INT8
+ * activations (M * K), their scales and code sums (M * 4 each), and, when the shape's output
+ * tiles leave compute units idle and K is split into S slices, the slices' int32 sums
+ * (S * M * N * 4); each part 256-byte aligned. 0 for M = 0 or bad shapes. */
 size_t w4a16_w4a8_workspace_bytes(int M, int K, int N);
+
+/* Name of the W4A8 GEMM configuration a shape gets ("w4a8_64x256", "w4a8_128x512", with
+ * "_splitk" when K is split); "none" for bad shapes. */
+const char* w4a16_w4a8_kernel_name(int M, int K, int N);
 
 /* W4A8: INT4 weights with per-token INT8 activations on the integer MFMA ("INT4 LLMs: What
  * 4-Bit Quantization Means…", weight-only section: [-8, 7] weights unpacked to INT8, an
@@ -155,7 +161,9 @@ size_t w4a16_w4a8_workspace_bytes(int M, int K, int N);
  * counts).
  *   y[m][n] = sx[m] * sw[n] * sum_k xq[m][k] * (u[k][n] - 8)
  *   sx[m] = RN_f32(max_k |x[m][k]| / 127),  xq = clip(rint(RN_f32(x / sx)), -127, 127)
- * The integer sum is exact; the epilogue multiplies it by the two scales in fp32.
+ * The integer sum is exact; the epilogue multiplies it by the two scales in fp32. With K split,
+ * the slices' int32 sums are added exactly by a second kernel before the same epilogue, so the
+ * result does not depend on the split.
  *   x         [in]  act [M][K] (quantized per row by a first kernel into the workspace)
  *   packed    [in]  output of w4a16_pack of symmetric codes (u = q + 8, as for w4a16_gemm with
  *                   qzeros = NULL)

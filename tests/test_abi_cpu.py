@@ -116,6 +116,28 @@ def test_awq_rejects_bad_s_inv_and_sizes_its_workspace(L):
     assert awq_workspace_bytes(16, 4096, 4104, 128) == 0   # N % 16: no shape
 
 
+def test_w4a8_workspace_and_geometry(L):
+    from weight_only_int4_w4a16_amd import w4a8_workspace_bytes, w4a8_kernel_name
+
+    def a256(b):
+        return (b + 255) // 256 * 256
+    # xq (M K bytes), sx and xsum (M * 4 each), and with K split the S int32 partial sums
+    assert w4a8_workspace_bytes(2048, 8192, 28672) == a256(2048 * 8192) + 2 * a256(2048 * 4)
+    assert w4a8_kernel_name(2048, 8192, 28672) == "w4a8_128x512"
+    # 64 x 256 tiles: 1 x 56 = 56 of them, K (32 blocks) cut in 4 slices of 8
+    assert w4a8_kernel_name(64, 4096, 14336) == "w4a8_64x256_splitk"
+    assert w4a8_workspace_bytes(64, 4096, 14336) == a256(64 * 4096) + 2 * a256(64 * 4) + 4 * 64 * 14336 * 4
+    assert w4a8_kernel_name(256, 4096, 14336) == "w4a8_64x256_splitk"          # 224 tiles, S = 2
+    assert w4a8_workspace_bytes(256, 4096, 14336) == a256(256 * 4096) + 2 * a256(256 * 4) + 2 * 256 * 14336 * 4
+    assert w4a8_kernel_name(1, 1024, 256) == "w4a8_64x256"                      # 8 blocks: no split
+    assert w4a8_workspace_bytes(0, 4096, 4096) == 0
+    assert w4a8_workspace_bytes(16, 4100, 4096) == 0 and w4a8_kernel_name(16, 4100, 4096) == "none"
+    vp = ctypes.c_void_p
+    assert L.w4a16_gemm_w4a8(vp(16), 16, 4096, 4096, 0, vp(16), vp(16), vp(16), 0, None, 0, None) == 4
+    assert L.w4a16_gemm_w4a8(vp(16), 16, 4072, 4096, 0, vp(16), vp(16), vp(16), 0, vp(256), 1 << 30, None) == 2
+    assert L.w4a16_gemm_w4a8(vp(16), 16, 4096, 4096, 0, vp(16), None, vp(16), 0, vp(256), 1 << 30, None) == 1
+
+
 def test_nf4_requires_codebook(L):
     vp = ctypes.c_void_p
     st = L.w4a16_gemm_nf4(vp(16), 1, 4096, 4096, 0, vp(16), vp(16), None, 64, vp(16), 0,

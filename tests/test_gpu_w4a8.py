@@ -68,9 +68,9 @@ def test_quantize_act_bit_exact(M, K, act):
 
 SMALL = [
     (1, 1024, 256, "f16"),
-    (17, 2080, 512, "bf16"),      # ragged K: the last 128-block has one 32-k step
-    (64, 4096, 1024, "f16"),
-    (130, 2048, 768, "bf16"),
+    (17, 2080, 512, "bf16"),      # ragged K (the last 128-block has one 32-k step), K split in 2
+    (64, 4096, 1024, "f16"),      # K split in 4
+    (130, 2048, 768, "bf16"),     # K split in 2
     (600, 1024, 16384, "f16"),    # 128x512 tiles, last row tile ragged
     (257, 512, 44048, "bf16"),    # N not a multiple of the tile width
 ]
@@ -80,7 +80,7 @@ SMALL = [
 def test_w4a8_gemm_matches_oracle(M, K, N, act):
     import weight_only_int4_w4a16_amd as w4
     torch = torch_mod()
-    _announce(f"w4a8 M={M} K={K} N={N} {act} {w4.lib().w4a16_w4a8_workspace_bytes(M, K, N)}")
+    _announce(f"w4a8 M={M} K={K} N={N} {act} {w4.w4a8_kernel_name(M, K, N)}")
     seed = synth.seed_for(13, K // 32 + N // 16 + M, 0)
     W = synth.gaussian_weight(K, N, seed)
     q, s = oracle.quantize_rtn_sym(W, K, act)                 # one scale per output channel
@@ -97,8 +97,8 @@ def test_w4a8_gemm_matches_oracle(M, K, N, act):
         assert np.array_equal(y16, synth.f32_to_bf16_bits(y.astype(np.float32)))
 
 
-@pytest.mark.parametrize("M,K,N,act", [(256, 4096, 14336, "f16"), (2048, 8192, 28672, "bf16"),
-                                       (4096, 4096, 14336, "bf16")])
+@pytest.mark.parametrize("M,K,N,act", [(64, 4096, 14336, "f16"), (256, 4096, 14336, "f16"),
+                                       (2048, 8192, 28672, "bf16"), (4096, 4096, 14336, "bf16")])
 def test_w4a8_full_size_sampled_strips(M, K, N, act):
     torch = torch_mod()
     _announce(f"w4a8 full M={M} K={K} N={N} {act}")
@@ -141,12 +141,13 @@ def test_w4a8_against_w4a16_within_activation_bound(M, act):
 
 
 def test_w4a8_graph_replays_match_eager():
-    """The quantizer and both GEMM tiles captured in one HIP graph: replays equal the eager run
-    bit for bit."""
+    """The quantizer, both GEMM tiles and the split-K reduction captured in one HIP graph:
+    replays equal the eager run bit for bit."""
     import weight_only_int4_w4a16_amd as w4
     torch = torch_mod()
     calls, outs = [], []
-    for i, (M, K, N, act) in enumerate([(64, 2048, 1024, "f16"), (600, 1024, 16384, "bf16")]):
+    for i, (M, K, N, act) in enumerate([(64, 2048, 1024, "f16"), (600, 1024, 16384, "bf16"),
+                                        (130, 4096, 2048, "f16")]):   # the last with K split
         _announce(f"w4a8 graph M={M} K={K} N={N} {act}")
         qw, _, _ = synth.timing_weights(K, N, 128, 100 + i, symmetric=True, scale_dtype=act)
         sw = synth.random_scales(1, N, 110 + i, act).reshape(-1)

@@ -8,10 +8,10 @@ does not load the library; the first call does, and raises if it was not built.
 """
 from .binding import (W4A16Error, F16, BF16, F32, lib, packed_bytes, workspace_bytes,
                       awq_workspace_bytes, w4a8_workspace_bytes, pack, gemm, gemm_nf4, gemm_awq,
-                      gemm_w4a8, quantize_act_int8, gemm_swiglu, gemm_nf4_swiglu, dequant,
+                      gemm_w4a8, w4a8_kernel_name, quantize_act_int8, gemm_swiglu, gemm_nf4_swiglu, dequant,
                       dequant_nf4, kernel_name, version)
 
 __all__ = ["W4A16Error", "F16", "BF16", "F32", "lib", "packed_bytes", "workspace_bytes",
            "awq_workspace_bytes", "w4a8_workspace_bytes", "pack", "gemm", "gemm_nf4", "gemm_awq",
-           "gemm_w4a8", "quantize_act_int8", "gemm_swiglu", "gemm_nf4_swiglu", "dequant", "dequant_nf4", "kernel_name",
+           "gemm_w4a8", "w4a8_kernel_name", "quantize_act_int8", "gemm_swiglu", "gemm_nf4_swiglu", "dequant", "dequant_nf4", "kernel_name",
            "version"]

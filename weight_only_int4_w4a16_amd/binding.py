@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_w4a8_workspace_bytes.restype = sz
     L.w4a16_gemm_w4a8.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
     L.w4a16_gemm_w4a8.restype = i32
+    L.w4a16_w4a8_kernel_name.argtypes = [i32, i32, i32]
+    L.w4a16_w4a8_kernel_name.restype = ctypes.c_char_p
     L.w4a16_quantize_act_int8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     L.w4a16_quantize_act_int8.restype = i32
     L.w4a16_gemm_swiglu.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
@@ -243,6 +245,10 @@ def gemm_w4a8(x, packed, wscale, out_dtype=None, out=None, workspace=None):
                                0 if ws is None else ws.numel() * ws.element_size(), _stream(x))
     _check(st, "w4a16_gemm_w4a8")
     return out
+
+
+def w4a8_kernel_name(M: int, K: int, N: int) -> str:
+    return lib().w4a16_w4a8_kernel_name(M, K, N).decode()
 
 
 def quantize_act_int8(x):

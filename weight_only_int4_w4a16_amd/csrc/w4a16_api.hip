@@ -139,7 +139,12 @@ w4a16_status w4a16_gemm_awq(const void* x, const void* s_inv, int M, int K, int 
 
 size_t w4a16_w4a8_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || K <= 0 || N <= 0 || K % 32 || N % 16 || (long long)K * N >= (1LL << 34)) return 0;
-  return w4a16::w4a8_workspace_bytes(M, K);
+  return w4a16::w4a8_workspace_bytes(M, K, N);
+}
+
+const char* w4a16_w4a8_kernel_name(int M, int K, int N) {
+  if (M <= 0 || K <= 0 || N <= 0 || K % 32 || N % 16) return "none";
+  return w4a16::w4a8_name(M, K, N);
 }
 
 w4a16_status w4a16_gemm_w4a8(const void* x, int M, int K, int N, w4a16_dtype act,
@@ -154,7 +159,7 @@ w4a16_status w4a16_gemm_w4a8(const void* x, int M, int K, int N, w4a16_dtype act
   if (!x || !packed || !wscale || !out) return W4A16_ERR_ARG;
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(out, 16) || !aligned(wscale, 2))
     return W4A16_ERR_ARG;
-  const size_t need = w4a16::w4a8_workspace_bytes(M, K);
+  const size_t need = w4a16::w4a8_workspace_bytes(M, K, N);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
   GemmArgs a{};
   a.x = x; a.M = M; a.K = K; a.N = N;

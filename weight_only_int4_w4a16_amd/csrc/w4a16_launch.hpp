@@ -62,8 +62,8 @@ size_t tiled_awq_workspace_bytes(int M, int K, int N);
 hipError_t launch_quantize_act(const void* x, int M, int K, int act, bool perm, int8_t* xq,
                                float* sx, int* xsum, hipStream_t s);
 hipError_t launch_w4a8(const GemmArgs& a);
-size_t w4a8_workspace_bytes(int M, int K);
-const char* w4a8_name(int M, int N);
+size_t w4a8_workspace_bytes(int M, int K, int N);
+const char* w4a8_name(int M, int K, int N);
 // x'[rows][K] = RN(x * s_inv[k]) (act dtype) into out, 16-byte aligned, K % 8 == 0
 hipError_t launch_awq_scale(const void* x, const void* s_inv, int rows, int K, int act, void* out,
                             hipStream_t stream);

@@ -146,6 +146,8 @@ struct W4A8Params {
   int M, K, N, KC, NT;
   int tiles_m, tiles_n;
   int act;
+  int S, kps;           // K slices (blockIdx.y) and k-blocks per slice
+  int* partials;        // S > 1: [S][M][N] int32 sums of xq * u, summed by the reduce kernel
 };
 
 template <class T>
@@ -161,6 +163,8 @@ __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
   const int tm = t % p.tiles_m, tn = t / p.tiles_m;  // neighbours share weight columns
   const int K = p.K, M = p.M, KC = p.KC;
   const int m0 = tm * kBM;
+  const int z = blockIdx.y;                      // K slice
+  const int kc0 = z * p.kps, kc1 = min(kc0 + p.kps, KC);
   const int nt0 = tn * (kWaves * 4) + wave * 4;  // this wave's first strip
   const int h = lane >> 5;
 
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         const int nt = min(nt0 + 2 * pr + ((lane >> 4) & 1), p.NT - 1);  // past N: never stored
-        const u4_t* blk = p.packed + ((size_t)nt * KC + min(kc + d, KC - 1)) * 64 + 32 * h + (lane & 15);
+        const u4_t* blk = p.packed + ((size_t)nt * KC + min(kc + d, kc1 - 1)) * 64 + 32 * h + (lane & 15);
         R.b[d][pr][0] = __builtin_nontemporal_load(blk);
         R.b[d][pr][1] = __builtin_nontemporal_load(blk + 16);
       }
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
     for (int i = 0; i < kAChunks; ++i) {
       const int c = threadIdx.x + kThreads * i;
       const int row = c / kCPR, kch = c % kCPR;
-      const bool in_k = R.kc * 128 + kch * 16 < K;
+      const bool in_k = R.kc * 128 + kch * 16 < min(K, kc1 * 128);  // this slice's k only
       *reinterpret_cast<u4_t*>(lds_q + buf * kBM * kARow + row * kARow + kch * 16) =
           in_k ? R.a[i] : u4_t{0u, 0u, 0u, 0u};
     }
@@ -243,19 +247,19 @@ __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
   };
 
   // two register sets and two LDS buffers: stage i+1 loads while stage i is multiplied
-  const int nb = (KC + kKB - 1) / kKB;
+  const int nb = (kc1 - kc0 + kKB - 1) / kKB;
   Regs R0, R1;
-  load(R0, 0);
+  load(R0, kc0);
   store_a(R0, 0);
   __syncthreads();
   int i = 0;
   for (; i + 1 < nb; i += 2) {
-    load(R1, (i + 1) * kKB);
+    load(R1, kc0 + (i + 1) * kKB);
     __builtin_amdgcn_sched_barrier(0);
     compute(R0, 0);
     store_a(R1, 1);
     __syncthreads();
-    load(R0, min(i + 2, nb - 1) * kKB);
+    load(R0, kc0 + min(i + 2, nb - 1) * kKB);
     __builtin_amdgcn_sched_barrier(0);
     compute(R1, 1);
     store_a(R0, 0);
@@ -281,6 +285,12 @@ __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
     for (int e = 0; e < 16; ++e) {
       const int m = m0 + mt * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
       if (m < M) {
+        if (p.S > 1) {  // K split: this slice's exact integer sums
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr)
+            if (in_n[pr]) p.partials[((size_t)z * M + m) * p.N + col[pr]] = acc[mt][pr][e];
+          continue;
+        }
         const int zs = 8 * p.xsum[m];
         const float sxm = p.sx[m];
 #pragma unroll
@@ -291,6 +301,27 @@ __global__ __launch_bounds__(T::kThreads) void w4a8_kernel(W4A8Params p) {
           }
       }
     }
+}
+
+// K split: the slices' integer sums add exactly (in any order), then the same epilogue as an
+// unsplit launch, so the result does not depend on S. Four consecutive columns per thread.
+__global__ __launch_bounds__(256) void w4a8_reduce_kernel(const int* __restrict__ partials, int M,
+                                                          int N, int S, const int* __restrict__ xsum,
+                                                          const float* __restrict__ sx,
+                                                          const uint16_t* __restrict__ wscale,
+                                                          int act, void* out, int out_dtype) {
+  const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= (size_t)M * N) return;
+  const int m = (int)(e / N), n = (int)(e - (size_t)m * N);
+  i4v_t v = *reinterpret_cast<const i4v_t*>(partials + e);
+  for (int zz = 1; zz < S; ++zz) v += *reinterpret_cast<const i4v_t*>(partials + (size_t)zz * M * N + e);
+  const int zs = 8 * xsum[m];
+  const float sxm = sx[m];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float sw = act == ACT_F16 ? act_value<ACT_F16>(wscale[n + c]) : act_value<ACT_BF16>(wscale[n + c]);
+    store_out(out, e + c, (float)(v[c] - zs) * sxm * sw, out_dtype);
+  }
 }
 
 int cu_count_w4a8() {
@@ -306,37 +337,59 @@ int cu_count_w4a8() {
   return v;
 }
 
-// the large tile when its tiles fill the compute units, else the small one
-bool w4a8_small(int M, int N) {
-  const int NT = N / 16;
+// Geometry: the large tile when its tiles fill the compute units, else the small one; and
+// while the small tiles leave compute units idle, K cut into S = 2, then 4 slices (each at
+// least 8 k-blocks).
+struct W4A8Geometry {
+  bool small;
+  int tiles_m, tiles_n, S, kps;
+};
+
+W4A8Geometry w4a8_geometry(int M, int K, int N) {
+  const int NT = N / 16, KC = ceil_div(K, 128), cus = cu_count_w4a8();
+  W4A8Geometry g;
   const long large = (long)ceil_div(M, I8Large::kBM) * ceil_div(NT, I8Large::kWaves * 4);
-  return large < cu_count_w4a8();
+  g.small = large < cus;
+  g.tiles_m = ceil_div(M, g.small ? I8Small::kBM : I8Large::kBM);
+  g.tiles_n = ceil_div(NT, (g.small ? I8Small::kWaves : I8Large::kWaves) * 4);
+  g.S = 1;
+  const long tiles = (long)g.tiles_m * g.tiles_n;
+  while (g.S < 4 && tiles * g.S < cus && KC >= 2 * g.S * 8) g.S *= 2;
+  g.kps = ceil_div(KC, g.S);
+  g.S = ceil_div(KC, g.kps);
+  return g;
 }
 
 struct W4A8Workspace {
-  size_t xq, sx, xsum, total;
+  size_t xq, sx, xsum, partials, total;
 };
 
-W4A8Workspace w4a8_layout(int M, int K) {
+W4A8Workspace w4a8_layout(int M, int K, int N) {
+  const W4A8Geometry g = w4a8_geometry(M, K, N);
   W4A8Workspace w;
   w.xq = 0;
   w.sx = align256((size_t)M * K);
   w.xsum = w.sx + align256((size_t)M * 4);
-  w.total = w.xsum + align256((size_t)M * 4);
+  w.partials = w.xsum + align256((size_t)M * 4);
+  w.total = w.partials + (g.S > 1 ? align256((size_t)g.S * M * N * 4) : 0);
   return w;
 }
 
 template <class T>
 hipError_t launch_w4a8_tile(const W4A8Params& p, hipStream_t s) {
-  hipLaunchKernelGGL(w4a8_kernel<T>, dim3(p.tiles_m * p.tiles_n), dim3(T::kThreads), T::kLdsBytes, s, p);
+  hipLaunchKernelGGL(w4a8_kernel<T>, dim3(p.tiles_m * p.tiles_n, p.S), dim3(T::kThreads), T::kLdsBytes, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t w4a8_workspace_bytes(int M, int K) { return M > 0 ? w4a8_layout(M, K).total : 0; }
+size_t w4a8_workspace_bytes(int M, int K, int N) { return M > 0 ? w4a8_layout(M, K, N).total : 0; }
 
-const char* w4a8_name(int M, int N) { return w4a8_small(M, N) ? "w4a8_64x256" : "w4a8_128x512"; }
+const char* w4a8_name(int M, int K, int N) {
+  const W4A8Geometry g = w4a8_geometry(M, K, N);
+  if (g.small) return g.S > 1 ? "w4a8_64x256_splitk" : "w4a8_64x256";
+  return g.S > 1 ? "w4a8_128x512_splitk" : "w4a8_128x512";
+}
 
 hipError_t launch_quantize_act(const void* x, int M, int K, int act, bool perm, int8_t* xq,
                                float* sx, int* xsum, hipStream_t s) {
@@ -353,7 +406,8 @@ hipError_t launch_quantize_act(const void* x, int M, int K, int act, bool perm, 
 }
 
 hipError_t launch_w4a8(const GemmArgs& a) {
-  const W4A8Workspace w = w4a8_layout(a.M, a.K);
+  const W4A8Geometry g = w4a8_geometry(a.M, a.K, a.N);
+  const W4A8Workspace w = w4a8_layout(a.M, a.K, a.N);
   char* ws = static_cast<char*>(a.workspace);
   W4A8Params p;
   p.xq = reinterpret_cast<const int8_t*>(ws + w.xq);
@@ -373,14 +427,17 @@ hipError_t launch_w4a8(const GemmArgs& a) {
   p.KC = ceil_div(a.K, 128);
   p.NT = a.N / 16;
   p.act = a.act;
-  if (w4a8_small(a.M, a.N)) {
-    p.tiles_m = ceil_div(a.M, I8Small::kBM);
-    p.tiles_n = ceil_div(p.NT, I8Small::kWaves * 4);
-    return launch_w4a8_tile<I8Small>(p, a.stream);
-  }
-  p.tiles_m = ceil_div(a.M, I8Large::kBM);
-  p.tiles_n = ceil_div(p.NT, I8Large::kWaves * 4);
-  return launch_w4a8_tile<I8Large>(p, a.stream);
+  p.tiles_m = g.tiles_m;
+  p.tiles_n = g.tiles_n;
+  p.S = g.S;
+  p.kps = g.kps;
+  p.partials = g.S > 1 ? reinterpret_cast<int*>(ws + w.partials) : nullptr;
+  e = g.small ? launch_w4a8_tile<I8Small>(p, a.stream) : launch_w4a8_tile<I8Large>(p, a.stream);
+  if (e != hipSuccess || g.S == 1) return e;
+  const size_t quads = (size_t)a.M * a.N / 4;
+  hipLaunchKernelGGL(w4a8_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, a.stream,
+                     p.partials, a.M, a.N, g.S, p.xsum, p.sx, p.wscale, a.act, a.out, a.out_dtype);
+  return hipGetLastError();
 }
 
 }  // namespace w4a16
