@@ -497,6 +497,22 @@ def test_awq_alpha_zero_is_rtn_and_scales_normalised():
     assert sv[order[-1]] / sv[order[0]] == pytest.approx(np.sqrt(a.max() / a.min()), rel=2e-3)
 
 
+def test_awq_silent_channel_keeps_a_finite_scale():
+    # a channel whose calibration activations are all zero gets the floor 1e-8 of the largest
+    # mean |x|, so its scale stays finite and the search still runs (its weight row is scaled
+    # down, which costs nothing: it never meets a nonzero activation)
+    rng = np.random.default_rng(25)
+    X = rng.normal(0, 1, (64, 32))
+    X[:, 5] = 0.0
+    for alpha in (0.0, 0.5, 0.95):
+        s_inv = oracle.awq.candidate_scales(X, alpha).astype(np.float64)
+        assert np.all(np.isfinite(s_inv)) and np.all(s_inv > 0)
+    assert s_inv[5] == s_inv.max()          # the smallest s, the largest S^-1
+    W = rng.normal(0, 0.05, (32, 16))
+    quant, s_inv, alpha, errs = oracle.awq.awq_quantize(W, X, 32, n_grid=4)
+    assert np.all(np.isfinite(errs)) and min(errs) <= errs[0]
+
+
 def test_awq_amplified_weight_has_a_smaller_effective_error():
     # section 3.2: with the group's step unchanged, a weight scaled by s before rounding and
     # divided by s after has at most half a step / s of error. The group's range is fixed
