@@ -61,9 +61,14 @@ def algo_bytes(M, K, N, g, zeros, nf4=False, act_bytes=2, out_bytes=2):
 
 
 def source_hash() -> str:
+    """Hash of the sources that define the decode kernel and its launch geometry (the kernel
+    the committed HBM-traffic counters were taken on); the dispatch that picks it is checked
+    separately, by kernel name."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "weight_only_int4_w4a16_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not (f.startswith("w4a16_decode") or f in ("w4a16_device.hpp", "w4a16_launch.hpp")):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -69,7 +69,7 @@ size_t w4a16_packed_bytes(int K, int N);
 w4a16_status w4a16_pack(const int32_t* qweight, int K, int N, int32_t* packed, void* stream);
 
 /* Bytes of scratch device memory w4a16_gemm / w4a16_gemm_nf4 need for this shape on the
- * current device: zero for the decode kernel (M <= 16); for the batched kernel (M > 16)
+ * current device: zero for the decode kernel (M <= 16, see w4a16_gemm); for the batched kernel
  * zero unless it splits K across workgroups, then the fp32 partial tiles of the K slices
  * (summed in slice order by a second kernel on the same stream). The caller allocates it;
  * it needs no initialization and holds nothing between calls. Calls that may run
@@ -86,7 +86,9 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group_size);
  *                   aligned (may be NULL when that size is 0)
  * M = 0 is a no-op. Results are deterministic: partial sums are combined in a fixed
  * order, never with floating-point atomics. M <= 16 runs the memory-bound decode kernel,
- * M > 16 the batched MFMA kernel (w4a16_kernel_name names the one a shape gets). */
+ * M > 16 the batched MFMA kernel; so do 12 <= M <= 16 on weights with K * N >= 2^27 whose
+ * activations do not fit the decode kernel's LDS staging (w4a16_kernel_name names the kernel
+ * a shape gets). */
 w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
                         const int32_t* packed, const void* scales, const int32_t* qzeros,
                         int group_size, void* out, w4a16_dtype out_dtype, void* workspace,

@@ -138,6 +138,17 @@ def test_w4a8_workspace_and_geometry(L):
     assert L.w4a16_gemm_w4a8(vp(16), 16, 4096, 4096, 0, vp(16), None, vp(16), 0, vp(256), 1 << 30, None) == 1
 
 
+def test_dispatch_between_decode_and_batched_kernels(L):
+    from weight_only_int4_w4a16_amd import kernel_name
+    assert kernel_name(16, 4096, 28672, 128).startswith("w4a16_decode")    # x fits in LDS
+    assert kernel_name(16, 14336, 4096, 128).startswith("w4a16_decode")    # K N < 2^27
+    assert kernel_name(16, 8192, 10240, 128).startswith("w4a16_decode")
+    assert kernel_name(11, 8192, 57344, 128).startswith("w4a16_decode")    # fewer than 12 rows
+    assert kernel_name(12, 8192, 57344, 128).startswith("w4a16_tiled")
+    assert kernel_name(16, 28672, 8192, 128).startswith("w4a16_tiled")
+    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_tiled")
+
+
 def test_nf4_requires_codebook(L):
     vp = ctypes.c_void_p
     st = L.w4a16_gemm_nf4(vp(16), 1, 4096, 4096, 0, vp(16), vp(16), None, 64, vp(16), 0,

@@ -332,6 +332,9 @@ FULL.append((2048, 8192, 28672, 128, "bf16", "asym"))                       # pr
 FULL.append((257, 2080, 44048, 32, "f16", "asym"))
 FULL.append((513, 2080, 44048, 32, "f16", "asym"))
 FULL.append((129, 4224, 28688, 64, "bf16", "asym"))
+# 12..16 rows on large weights whose x exceeds the decode kernel's LDS: the batched kernel
+FULL.append((16, 8192, 57344, 128, "f16", "sym"))
+FULL.append((12, 28672, 8192, 128, "bf16", "asym"))
 
 
 @pytest.mark.parametrize("M,K,N,g,act,fmt", FULL)

@@ -27,7 +27,16 @@ w4a16_status from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_
 // M above 16 goes to the batched kernel: past one 16-row MFMA tile the decode kernel's
 // activation traffic per weight byte outgrows the batched kernel's dequantization cost
 // (4096x14336: M=32 takes 33.7 us on the decode kernel, M=64 24.8 us on the batched one)
-bool use_tiled(const GemmArgs& a) { return a.M > 16 && w4a16::tiled_supported(a); }
+// The exception: from 12 rows on, a large weight (K N >= 2^27) whose x does not fit the decode
+// kernel's LDS staging (so every workgroup re-reads x from L2 with each group) runs faster on
+// the batched kernel (M=16: 8192x57344 118 -> 101 us, 28672x8192 58.7 -> 50.7 us; smaller
+// weights such as 8192x10240 and 14336x4096 stay faster on the decode kernel).
+bool use_tiled(const GemmArgs& a) {
+  if (!w4a16::tiled_supported(a)) return false;
+  if (a.M > 16) return true;
+  if (a.M < 12 || (long long)a.K * a.N < (1LL << 27)) return false;
+  return !w4a16::decode_config(a.M, a.K, a.N, a.group_size, a.glu).x_in_lds;
+}
 
 size_t workspace_need(int M, int K, int N, int gs) {
   GemmArgs a{};
