@@ -86,9 +86,10 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group_size);
  *                   aligned (may be NULL when that size is 0)
  * M = 0 is a no-op. Results are deterministic: partial sums are combined in a fixed
  * order, never with floating-point atomics. M <= 16 runs the memory-bound decode kernel,
- * M > 16 the batched MFMA kernel; so do 12 <= M <= 16 on weights with K * N >= 2^27 whose
- * activations do not fit the decode kernel's LDS staging (w4a16_kernel_name names the kernel
- * a shape gets). */
+ * M > 16 the batched MFMA kernel, with two exceptions: 12 <= M <= 16 on weights with
+ * K * N >= 2^27 whose activations do not fit the decode kernel's LDS staging go to the batched
+ * kernel, and 17 <= M <= 32 on weights with K * N <= 2^24 stay on the decode kernel (one launch
+ * per 16 rows). w4a16_kernel_name names the kernel a shape gets. */
 w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
                         const int32_t* packed, const void* scales, const int32_t* qzeros,
                         int group_size, void* out, w4a16_dtype out_dtype, void* workspace,

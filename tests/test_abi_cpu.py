@@ -146,7 +146,10 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     assert kernel_name(11, 8192, 57344, 128).startswith("w4a16_decode")    # fewer than 12 rows
     assert kernel_name(12, 8192, 57344, 128).startswith("w4a16_tiled")
     assert kernel_name(16, 28672, 8192, 128).startswith("w4a16_tiled")
-    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_tiled")
+    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_decode")     # K N <= 2^24
+    assert kernel_name(32, 4096, 4096, 128).startswith("w4a16_decode")
+    assert kernel_name(33, 4096, 4096, 128).startswith("w4a16_tiled")
+    assert kernel_name(17, 4096, 6144, 128).startswith("w4a16_tiled")
 
 
 def test_nf4_requires_codebook(L):
@@ -177,7 +180,10 @@ def test_kernel_name_and_strings(L):
                        (16, 4096, 28672, 128)):
         assert kernel_name(M, K, N, g).endswith("_persist"), (M, K, N, g)
     assert not kernel_name(1, 4096, 28672, 128).endswith("_persist")
-    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_tiled")
+    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_decode")     # K N <= 2^24
+    assert kernel_name(32, 4096, 4096, 128).startswith("w4a16_decode")
+    assert kernel_name(33, 4096, 4096, 128).startswith("w4a16_tiled")
+    assert kernel_name(17, 4096, 6144, 128).startswith("w4a16_tiled")
     assert kernel_name(65, 4096, 4096, 128).startswith("w4a16_tiled")
     # the ragged full-size parity shapes land on each batched geometry (256 compute units)
     assert kernel_name(257, 2080, 44048, 32) == "w4a16_tiled_64x256"

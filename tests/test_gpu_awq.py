@@ -64,7 +64,8 @@ SMALL = [
     (16, 2048, 1024, 32, "f16", "asym"),
     (9, 9216, 256, 128, "f16", "asym"),     # x does not fit in LDS: scaled into the workspace
     (16, 8320, 512, 64, "bf16", "asym"),
-    (17, 1024, 768, 128, "f16", "asym"),    # batched, just past one decode tile
+    (17, 1024, 768, 128, "f16", "asym"),    # decode, two launches (16 + 1 rows)
+    (20, 4096, 4128, 128, "bf16", "asym"),  # batched 64x256 tile, just past 16 rows
     (40, 2080, 512, 32, "bf16", "sym"),
     (130, 2048, 64, 128, "f16", "asym"),    # batched, K split in two
 ]

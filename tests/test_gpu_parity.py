@@ -87,10 +87,13 @@ SMALL = [
     (9, 4224, 48, 64, "bf16", "sym"),
     (16, 8320, 32, 32, "f16", "asym"),
     (16, 1024, 48, 64, "bf16", "asym"),
-    # just past the decode kernel: one ragged 64-row tile of the batched kernel
+    # 17..32 rows on small weights (K N <= 2^24): the decode kernel, one launch per 16 rows
     (17, 512, 64, 128, "bf16", "asym"),
     (32, 1024, 48, 64, "bf16", "asym"),
     (20, 8320, 32, 32, "f16", "asym"),
+    # just past 16 rows on larger weights: one ragged 64-row tile of the batched kernel
+    (17, 4096, 4112, 128, "f16", "asym"),
+    (24, 2048, 8208, 64, "bf16", "sym"),
     (50, 8192, 32, 128, "f16", "asym"),
     # persistent decode workgroups (more tiles than resident slots, x staged once): one and
     # two strips per tile, waves with one group and with several, a ragged K, g32
@@ -148,7 +151,8 @@ SWIGLU = [
     (12, 4096, 16416, 128, "f16", "asym"),   # persistent, one group per wave
     (9, 4224, 16448, 64, "bf16", "nf4"),     # persistent, several groups per wave
     (2, 1024, 96, 64, "bf16", "nf4"),
-    (17, 512, 64, 128, "bf16", "asym"),      # batched 64x256, K split
+    (17, 512, 64, 128, "bf16", "asym"),      # decode, two launches (16 + 1 rows)
+    (20, 4096, 4128, 128, "bf16", "asym"),   # batched 64x256, K split
     (130, 2144, 96, 32, "f16", "sym"),
     (300, 1024, 544, 128, "f16", "asym"),    # batched 64x256, ragged tile
     (257, 2080, 2080, 32, "f16", "nf4"),

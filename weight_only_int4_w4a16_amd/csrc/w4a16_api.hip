@@ -31,9 +31,12 @@ w4a16_status from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_
 // kernel's LDS staging (so every workgroup re-reads x from L2 with each group) runs faster on
 // the batched kernel (M=16: 8192x57344 118 -> 101 us, 28672x8192 58.7 -> 50.7 us; smaller
 // weights such as 8192x10240 and 14336x4096 stay faster on the decode kernel).
+// Small weights (K N <= 2^24) keep the decode kernel, in 16-row launches, up to 32 rows: their
+// batched tiles cannot fill the chip (4096x4096: M=17 15.8 -> 11.3 us, M=32 17.7 -> 14.5 us).
 bool use_tiled(const GemmArgs& a) {
   if (!w4a16::tiled_supported(a)) return false;
-  if (a.M > 16) return true;
+  if (a.M > 32) return true;
+  if (a.M > 16) return (long long)a.K * a.N > (1LL << 24);
   if (a.M < 12 || (long long)a.K * a.N < (1LL << 27)) return false;
   return !w4a16::decode_config(a.M, a.K, a.N, a.group_size, a.glu).x_in_lds;
 }
