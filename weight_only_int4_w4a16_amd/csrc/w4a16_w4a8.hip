@@ -24,6 +24,9 @@
 // pairs of strips) over all the tile's rows. In the 32x32x32 operands lane l holds row / column
 // l % 32 and k = 16 (l / 32) .. +16 of a 32-k step; for the B operand those 16 codes are word
 // s of the packed block's chunks 32 (l / 32) + l % 16 and that + 16, which lane l loads itself.
+// When the output tiles leave compute units idle, K is split into 2 or 4 slices whose exact
+// int32 sums a third small kernel adds before the same epilogue (the result does not depend on
+// the split).
 #include <type_traits>
 
 #include "w4a16_device.hpp"
