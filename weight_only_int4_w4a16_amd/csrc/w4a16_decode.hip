@@ -117,6 +117,18 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu
     }
   }
   if (rows >= 8 && best_rounds > 1 && pbest_cost >= 0) return pbest;
+  // One row of x, and a wave that would stream more than 8 groups one after another: twice the
+  // waves on half the slice each, when every workgroup still fits at once. The model above
+  // counts 16 resident waves per compute unit; these 60-register instantiations fit 32, and
+  // with x this small LDS does not limit them (8192x57344: 2 -> 4 waves, 47 -> 44 us).
+  if (rows == 1 && x_in_lds && best.W * 2 <= wmax) {
+    const int D = decode_group_blocks(best.SW, GPC, x_in_lds);
+    if (ceil_div(best.slice, D) > 8) {
+      DecodeConfig c = geometry(M, K, N, x_in_lds, best.SW, best.W * 2);
+      c.glu = glu;
+      if (c.lds_bytes * (32 / c.W) <= kMaxLds && c.tiles <= (long)cus * (32 / c.W)) return c;
+    }
+  }
   return best;
 }
 
