@@ -167,7 +167,7 @@ const char* w4a16_w4a8_kernel_name(int M, int K, int N);
  * The integer sum is exact; the epilogue multiplies it by the two scales in fp32. With K split,
  * the slices' int32 sums are added exactly by a second kernel before the same epilogue, so the
  * result does not depend on the split.
- *   x         [in]  act [M][K] (quantized per row by a first kernel into the workspace)
+ *   x         [in]  act [M][K], finite (quantized per row by a first kernel into the workspace)
  *   packed    [in]  output of w4a16_pack of symmetric codes (u = q + 8, as for w4a16_gemm with
  *                   qzeros = NULL)
  *   wscale    [in]  act [N], one scale per output channel
