@@ -84,10 +84,10 @@ constexpr int decode_group_blocks(int SW, int GPC, bool XL) {
   return XL ? (GPC == 4 || (GPC == 2 && SW == 2) ? 2 : 4) / SW : 1;
 }
 
-// fp16 affine formats multiply integer-valued operands and
-// apply the group scale to the fp32 partial sums; otherwise W_hat is formed in registers
-// with its one rounding to the activation type.
-constexpr bool decode_defers_scale(int ACT, int FMT) { return ACT == 0 && FMT != 2; }
+// fp16 activations: the affine formats multiply integer-valued operands and NF4 the bare
+// codebook levels, and the group scale (absmax) is applied to the fp32 partial sums; with bf16
+// activations W_hat is formed in registers with its one rounding to the activation type.
+constexpr bool decode_defers_scale(int ACT, int FMT) { return ACT == 0; }
 
 // workgroup -> tile: tiles [start(x), start(x) + count(x)) run on XCD x = blockIdx % 8
 __device__ __forceinline__ int tile_of(int b, int G) {
@@ -224,25 +224,32 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
                 for (int mt = 0; mt < MT; ++mt) acc[sw][mt] = mfma16(a[mt], bf, acc[sw][mt]);
               }
             } else {
-              // affine: integer-valued operands into the group's partial sum, scaled once
-              // when the group's last 32-k step is done
+              // integer-valued operands (affine) or the bare codebook levels (NF4) into the
+              // group's partial sum, scaled once when the group's last 32-k step is done
               const bool first = j % SPG == 0, last = j % SPG == SPG - 1;
 #pragma unroll
               for (int sw = 0; sw < SW; ++sw) {
                 const uint32_t w = b[d][sw][j];
-                const uint32_t zq = ZEROS ? (z[d][sw][gi] >> shift) & 0xFu : 8u;
-                AT bq, bz;
-                if constexpr (ACT == ACT_F16) {
-                  bq = unpack_biased_f16(w);
-                  bz = neg_bias_f16(zq);
-                } else {
-                  bq = unpack_biased_bf16(w);
-                  bz = neg_bias_bf16(zq);
-                }
+                if constexpr (FMT == FMT_NF4) {
+                  const AT bq = nf4_levels_f16(w, lut);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                  part[sw][mt] = mfma16(a[mt], bq, first ? f4_t{0.f, 0.f, 0.f, 0.f} : part[sw][mt]);
-                  part[sw][mt] = mfma16(a[mt], bz, part[sw][mt]);
+                  for (int mt = 0; mt < MT; ++mt)
+                    part[sw][mt] = mfma16(a[mt], bq, first ? f4_t{0.f, 0.f, 0.f, 0.f} : part[sw][mt]);
+                } else {
+                  const uint32_t zq = ZEROS ? (z[d][sw][gi] >> shift) & 0xFu : 8u;
+                  AT bq, bz;
+                  if constexpr (ACT == ACT_F16) {
+                    bq = unpack_biased_f16(w);
+                    bz = neg_bias_f16(zq);
+                  } else {
+                    bq = unpack_biased_bf16(w);
+                    bz = neg_bias_bf16(zq);
+                  }
+#pragma unroll
+                  for (int mt = 0; mt < MT; ++mt) {
+                    part[sw][mt] = mfma16(a[mt], bq, first ? f4_t{0.f, 0.f, 0.f, 0.f} : part[sw][mt]);
+                    part[sw][mt] = mfma16(a[mt], bz, part[sw][mt]);
+                  }
                 }
                 if (last) {
                   const uint32_t sraw = s[d][sw][gi];

@@ -1,9 +1,9 @@
 // w4a16_device.hpp - device-side building blocks shared by every W4A16 kernel on gfx950:
 // the private packed weight layout, nibble unpacking, the one-rounding dequantization and
 // thin MFMA wrappers. Every kernel that forms W_hat calls the routines below, so the
-// dequant test hook and the GEMMs compute bit-identical weights. (The fp16 affine decode
-// kernel instead multiplies the exact integers q - z and scales the fp32 group sums; see
-// unpack_biased_f16.)
+// dequant test hook and the GEMMs compute bit-identical weights. (The fp16 decode kernel
+// instead multiplies the exact integers q - z, or the bare NF4 levels, and scales the fp32
+// group sums; see unpack_biased_f16 and nf4_levels_f16.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -211,6 +211,19 @@ __device__ inline void lut16_half(const Nf4Lut& L, uint32_t idx, uint32_t& h01, 
   const uint32_t hi = lut16_bytes(L.hi, idx);
   h01 = perm_b32(hi, lo, 0x05010400u);  // bytes: lo0, hi0, lo1, hi1
   h23 = perm_b32(hi, lo, 0x07030602u);  // bytes: lo2, hi2, lo3, hi3
+}
+
+// The eight fp16 codebook levels of one packed word, in k order (no absmax): the operand of
+// the fp16 decode kernel, which applies the absmax to each block's fp32 partial sum.
+__device__ inline h8_t nf4_levels_f16(uint32_t w, const Nf4Lut& L) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t i0 = perm_b32(hi, lo, 0x06040200u);  // codes 0,1,2,3
+  const uint32_t i1 = perm_b32(hi, lo, 0x07050301u);  // codes 4,5,6,7
+  uint32_t c01, c23, c45, c67;
+  lut16_half(L, i0, c01, c23);
+  lut16_half(L, i1, c45, c67);
+  return __builtin_bit_cast(h8_t, u4_t{c01, c23, c45, c67});
 }
 
 __device__ inline h8_t dequant_word_nf4_f16(uint32_t w, const Nf4Lut& L, h2_t a2) {
