@@ -603,6 +603,24 @@ def test_w4a8_signed_codes_from_offset_binary():
     assert q[:16, 0].tolist() == list(range(-8, 8))
 
 
+def test_w4a8_reference_equals_python_loops():
+    # the whole W4A8 reference (per-token codes, unpacked offset-binary weights, integer sum,
+    # both scales) against plain Python arithmetic on a tiny case
+    rng = np.random.default_rng(46)
+    M, K, N = 3, 16, 8
+    x = rng.normal(0, 1, (M, K)).astype(np.float16)
+    u = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    sw = np.array(rng.uniform(0.01, 0.02, N), dtype=np.float16)
+    y = oracle.w4a8.gemm_w4a8_ref(x, oracle.pack_codes(u), sw, "f16")
+    for m in range(M):
+        xs = [float(v) for v in x[m]]
+        sx = float(np.float32(max(abs(v) for v in xs)) / np.float32(127))
+        q = [max(-127, min(127, int(np.rint(np.float32(v) / np.float32(sx))))) for v in xs]
+        for n in range(N):
+            acc = sum(q[k] * (int(u[k, n]) - 8) for k in range(K))
+            assert y[m, n] == acc * sx * float(sw[n])
+
+
 def test_w4a8_reduces_to_w4a16_when_x_is_on_the_int8_grid():
     # x = sx * xq exactly (integers with max 127, sx = 1) and power-of-two weight scales:
     # the W4A8 result equals the W4A16 oracle on the per-channel-scaled weight
