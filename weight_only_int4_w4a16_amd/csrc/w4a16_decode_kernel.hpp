@@ -109,6 +109,9 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   constexpr int SPG = 4 / GPC;        // 32-k steps per scale group
   constexpr bool ZEROS = FMT == FMT_ASYM;
   constexpr bool DEFER = decode_defers_scale(ACT, FMT);
+  // fp16 NF4 with x in LDS: x is staged with each group of eight k in the packed nibble order,
+  // so the codebook levels go into the MFMA without regrouping
+  constexpr bool XNIB = XL && DEFER && FMT == FMT_NF4;
 
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
               for (int sw = 0; sw < SW; ++sw) {
                 const uint32_t w = b[d][sw][j];
                 if constexpr (FMT == FMT_NF4) {
-                  const AT bq = nf4_levels_f16(w, lut);
+                  const AT bq = XNIB ? nf4_levels_f16_nibble_order(w, lut) : nf4_levels_f16(w, lut);
 #pragma unroll
                   for (int mt = 0; mt < MT; ++mt)
                     part[sw][mt] = mfma16(a[mt], bq, first ? f4_t{0.f, 0.f, 0.f, 0.f} : part[sw][mt]);
@@ -308,6 +311,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
       for (int i = 0; i < kXRegs; ++i) {
         u4_t v = xr[i];
         if constexpr (XS) v = scale_act8<ACT>(v, xsr[i]);
+        if constexpr (XNIB) v = act8_to_nibble_order(v);
         *reinterpret_cast<u4_t*>(xs + xoff[i]) = v;
       }
       // chunks beyond the register-staged ones (slices of several rows)
@@ -315,6 +319,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
         const int m = c / cpr, cc = c - (c / cpr) * cpr;
         u4_t v = *reinterpret_cast<const u4_t*>(p.x + (size_t)m * K + kbeg + cc * 8);
         if constexpr (XS) v = scale_act8<ACT>(v, *reinterpret_cast<const u4_t*>(p.xscale + kbeg + cc * 8));
+        if constexpr (XNIB) v = act8_to_nibble_order(v);
         *reinterpret_cast<u4_t*>(xs + (size_t)m * p.xstride + cc * 8) = v;
       }
     }

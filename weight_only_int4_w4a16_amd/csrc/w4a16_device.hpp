@@ -226,6 +226,22 @@ __device__ inline h8_t nf4_levels_f16(uint32_t w, const Nf4Lut& L) {
   return __builtin_bit_cast(h8_t, u4_t{c01, c23, c45, c67});
 }
 
+// The same levels in the word's nibble order, k = 0, 4, 1, 5, 2, 6, 3, 7 (no regrouping):
+// for a kernel whose activations are stored in that order too (the products and their sum
+// over the eight k are unchanged).
+__device__ inline h8_t nf4_levels_f16_nibble_order(uint32_t w, const Nf4Lut& L) {
+  uint32_t c04, c15, c26, c37;
+  lut16_half(L, w & 0x0F0F0F0Fu, c04, c15);          // codes 0, 4, 1, 5
+  lut16_half(L, (w >> 4) & 0x0F0F0F0Fu, c26, c37);   // codes 2, 6, 3, 7
+  return __builtin_bit_cast(h8_t, u4_t{c04, c15, c26, c37});
+}
+
+// Eight 16-bit activations (k order) rearranged to k = 0, 4, 1, 5, 2, 6, 3, 7.
+__device__ inline u4_t act8_to_nibble_order(u4_t v) {
+  return u4_t{perm_b32(v[2], v[0], 0x05040100u), perm_b32(v[2], v[0], 0x07060302u),
+              perm_b32(v[3], v[1], 0x05040100u), perm_b32(v[3], v[1], 0x07060302u)};
+}
+
 __device__ inline h8_t dequant_word_nf4_f16(uint32_t w, const Nf4Lut& L, h2_t a2) {
   // lo bytes: codes 0,4,1,5 ; hi bytes: codes 2,6,3,7 -> regroup to (0,1),(2,3),(4,5),(6,7)
   const uint32_t lo = w & 0x0F0F0F0Fu;
