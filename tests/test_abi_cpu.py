@@ -216,3 +216,87 @@ def test_synth_module_holds_no_method_arithmetic():
     src = open(os.path.join(ROOT, "weight_only_int4_w4a16_amd", "synth.py")).read()
     for banned in ("rint", "clip(", "matmul", "@", "dequant", "<< np.uint32(4"):
         assert banned not in src.split('"""', 2)[-1], banned
+
+
+# ---------------------------------------------------------------- binding tensor checks
+# The C ABI receives no buffer sizes, so the binding checks every tensor against the shape
+# the call implies before a pointer is taken. These run on CPU tensors: a well-shaped call
+# gets as far as the device check ("device tensors"); a mis-shaped one must stop earlier,
+# at the shape check.
+
+def _cpu_affine(M=4, K=256, N=64, g=128, dt=None, zeros=True):
+    import torch
+    from weight_only_int4_w4a16_amd import packed_bytes
+    dt = torch.float16 if dt is None else dt
+    return dict(x=torch.zeros((M, K), dtype=dt), packed=torch.zeros(packed_bytes(K, N) // 4, dtype=torch.int32),
+                scales=torch.zeros((K // g, N), dtype=dt),
+                qzeros=torch.zeros((K // g, N // 8), dtype=torch.int32) if zeros else None, g=g)
+
+
+def _raises_arg(fn, match):
+    from weight_only_int4_w4a16_amd import W4A16Error
+    with pytest.raises(W4A16Error, match=match) as e:
+        fn()
+    assert e.value.status == 1
+
+
+def test_binding_well_shaped_call_reaches_the_device_check():
+    import weight_only_int4_w4a16_amd as w4
+    a = _cpu_affine()
+    _raises_arg(lambda: w4.gemm(a["x"], a["packed"], a["scales"], a["qzeros"], a["g"]), "device tensors")
+
+
+@pytest.mark.parametrize("what", ["out_rows", "out_cols", "out_dtype", "scales_rows", "scales_dtype",
+                                  "qzeros_cols", "packed_short", "x_1d", "workspace_short"])
+def test_binding_gemm_rejects_wrong_shapes(what):
+    import torch
+    import weight_only_int4_w4a16_amd as w4
+    a = _cpu_affine(M=40, K=4096, N=4096)
+    kw = {}
+    if what == "out_rows":
+        kw["out"] = torch.zeros((39, 4096), dtype=torch.float16)
+    elif what == "out_cols":
+        kw["out"] = torch.zeros((40, 4080), dtype=torch.float16)
+    elif what == "out_dtype":
+        kw["out"] = torch.zeros((40, 4096), dtype=torch.bfloat16)
+    elif what == "scales_rows":
+        a["scales"] = torch.zeros((31, 4096), dtype=torch.float16)
+    elif what == "scales_dtype":
+        a["scales"] = torch.zeros((32, 4096), dtype=torch.float32)
+    elif what == "qzeros_cols":
+        a["qzeros"] = torch.zeros((32, 256), dtype=torch.int32)
+    elif what == "packed_short":
+        a["packed"] = a["packed"][:-1]
+    elif what == "x_1d":
+        a["x"] = torch.zeros(4096, dtype=torch.float16)
+    elif what == "workspace_short":
+        need = w4.workspace_bytes(40, 4096, 4096, 128)
+        assert need > 0
+        kw["workspace"] = torch.zeros(need - 1, dtype=torch.uint8)
+    _raises_arg(lambda: w4.gemm(a["x"], a["packed"], a["scales"], a["qzeros"], a["g"], **kw),
+                "shape|dtype|bytes|2-D")
+
+
+def test_binding_other_entry_points_reject_wrong_shapes():
+    import torch
+    import weight_only_int4_w4a16_amd as w4
+    from weight_only_int4_w4a16_amd import packed_bytes
+    a = _cpu_affine(M=2, K=512, N=64, g=64)
+    x, pk, sc, qz = a["x"], a["packed"], a["scales"], a["qzeros"]
+    absmax = torch.zeros((8, 64), dtype=torch.float16)
+    cb = torch.zeros(16, dtype=torch.float16)
+    m = "shape|dtype|bytes|2-D|even"
+    _raises_arg(lambda: w4.gemm_nf4(x, pk, absmax, torch.zeros(15, dtype=torch.float16), 64), m)
+    _raises_arg(lambda: w4.gemm_nf4(x, pk, absmax[:7], cb, 64), m)
+    _raises_arg(lambda: w4.gemm_nf4(x, pk, absmax, cb, 64, out=torch.zeros((2, 32), dtype=torch.float16)), m)
+    _raises_arg(lambda: w4.gemm_awq(x, torch.zeros(511, dtype=torch.float16), pk, sc, qz, 64), m)
+    _raises_arg(lambda: w4.gemm_awq(x, torch.zeros(512, dtype=torch.bfloat16), pk, sc, qz, 64), m)
+    _raises_arg(lambda: w4.gemm_swiglu(x, pk, sc, qz, 64, out=torch.zeros((2, 64), dtype=torch.float16)), m)
+    _raises_arg(lambda: w4.gemm_nf4_swiglu(x, pk, absmax, cb, 64, out=torch.zeros((2, 64), dtype=torch.float16)), m)
+    _raises_arg(lambda: w4.gemm_w4a8(x, pk, torch.zeros((64,), dtype=torch.float16),
+                                     out=torch.zeros((2, 63), dtype=torch.float16)), m)
+    _raises_arg(lambda: w4.gemm_w4a8(x, pk[:10], torch.zeros((64,), dtype=torch.float16)), m)
+    _raises_arg(lambda: w4.dequant(pk, sc[:3], qz, 512, 64), m)
+    _raises_arg(lambda: w4.dequant(pk[: packed_bytes(512, 64) // 8], sc, qz, 512, 64), m)
+    _raises_arg(lambda: w4.dequant_nf4(pk, absmax, cb[:8], 512, 64), m)
+    _raises_arg(lambda: w4.dequant_nf4(pk, absmax, cb, 512, 128), m)

@@ -700,6 +700,37 @@ def test_nf4_quantizer_picks_nearest_level_and_dequant():
     assert np.array_equal(w2.astype(np.float64), 2 * cv[codes])      # a = 2 -> exact double
 
 
+def test_nf4_dequant_block_index_hand_worked():
+    """"INT4 and Low-Bit Inference", section 5 (The formats): NF4 scales each block of 64
+    consecutive weights by its own absmax. Hand-worked: one column, two blocks with absmax
+    0.5 and 4; the codes at both ends of each block are the extreme levels (code 15 = +1,
+    code 0 = -1) or the zero level (code 7)."""
+    c = oracle.nf4_codebook()
+    codes = np.full((128, 1), 7, np.uint8)
+    codes[0, 0], codes[63, 0], codes[64, 0], codes[127, 0] = 15, 0, 15, 0
+    a = np.array([[0.5], [4.0]], np.float16)
+    w = oracle.dequant_nf4(oracle.pack_codes(codes), a, c, 64).astype(np.float64)[:, 0]
+    assert (w[0], w[63], w[64], w[127]) == (0.5, -0.5, 4.0, -4.0)
+    assert np.all(w[1:63] == 0) and np.all(w[65:127] == 0)
+
+
+@pytest.mark.parametrize("block", [32, 64, 128])
+def test_nf4_dequant_absmax_per_block_and_column(block):
+    """Every (block, column) gets a distinct power-of-two absmax; with code 15 (level +1)
+    everywhere, W_hat must repeat each absmax over exactly the `block` consecutive k of its
+    block, in its own column (a power of two times +1 is exact)."""
+    c = oracle.nf4_codebook()
+    K, N = 4 * block, 8
+    codes = np.full((K, N), 15, np.uint8)
+    e = np.arange(4)[:, None] * N + np.arange(N)[None, :]           # 32 distinct exponents
+    a = np.ldexp(1.0, e - 16).astype(np.float16)                    # 2^-16 .. 2^15
+    assert len(np.unique(a)) == 4 * N
+    w = oracle.dequant_nf4(oracle.pack_codes(codes), a, c, block).astype(np.float64)
+    for b in range(4):
+        for n in range(N):
+            assert np.all(w[b * block:(b + 1) * block, n] == float(a[b, n])), (b, n)
+
+
 # ---------------------------------------------------------------- roofline arithmetic
 
 def test_naive_path_bytes_and_ceiling():
