@@ -37,8 +37,18 @@ def common_flags() -> list:
             f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
+def _newest_header() -> float:
+    heads = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".h"))]
+    heads.append(os.path.join(ROOT, "include", "w4a16.h"))
+    return max(os.path.getmtime(h) for h in heads)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if incremental and os.path.exists(obj):
+        t = os.path.getmtime(obj)
+        if t > os.path.getmtime(os.path.join(CSRC, src)) and t > _newest_header():
+            return obj
     cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -46,10 +56,12 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every source (``incremental``: only those older than their object, or than a
+    header) and link the library."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda f: _compile(f, incremental), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -62,5 +74,5 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv[1:])
     sys.exit(0)
