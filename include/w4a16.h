@@ -122,6 +122,26 @@ w4a16_status w4a16_gemm_swiglu(const void* x, int M, int K, int N2, w4a16_dtype 
                                int group_size, void* out, w4a16_dtype out_dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Maximum scratch of w4a16_gemm_static, in bytes (a static device array on each GPU). */
+#define W4A16_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* w4a16_gemm for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels and results as
+ * w4a16_gemm, bit for bit, with the split-K scratch taken from a file-scope device array of
+ * W4A16_STATIC_SCRATCH_BYTES per GPU instead of a workspace argument. The array is held by
+ * each GPU the library runs on until the process ends; the first call on a device looks up
+ * its address (hipGetSymbolAddress). The call allocates and frees nothing.
+ *   Arguments, checks and errors as for w4a16_gemm, plus W4A16_ERR_WORKSPACE when the shape
+ *   needs more scratch than W4A16_STATIC_SCRATCH_BYTES (w4a16_workspace_bytes gives the
+ *   need), and W4A16_ERR_HIP when the array's address cannot be obtained.
+ * Every call on one GPU shares that GPU's array and the array keeps the last call's partial
+ * sums; nothing in it needs to start at zero (each call writes every partial it reads). Calls
+ * whose executions overlap on one GPU (different streams, or concurrent host threads) race
+ * on it and give wrong results: serialize them, or use w4a16_gemm with one workspace each. */
+w4a16_status w4a16_gemm_static(const void* x, int M, int K, int N, w4a16_dtype act,
+                               const int32_t* packed, const void* scales, const int32_t* qzeros,
+                               int group_size, void* out, w4a16_dtype out_dtype, void* stream);
+
 /* Bytes of scratch device memory w4a16_gemm_awq needs for this shape on the current device:
  * as w4a16_workspace_bytes, plus room for the scaled activations where they are formed by a
  * pre-pass: M * K * 2 bytes (256-byte multiples) for decode shapes (M <= 16) whose

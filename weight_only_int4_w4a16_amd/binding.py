@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_workspace_bytes.restype = sz
     L.w4a16_gemm.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
     L.w4a16_gemm.restype = i32
+    L.w4a16_gemm_static.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp]
+    L.w4a16_gemm_static.restype = i32
     L.w4a16_gemm_nf4.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
     L.w4a16_gemm_nf4.restype = i32
     L.w4a16_awq_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -285,6 +287,18 @@ def gemm(x, packed, scales, qzeros, group_size: int, out_dtype=None, out=None, w
                           _ptr(qzeros), group_size, _ptr(out), _dt(out.dtype), *_ws_args(ws),
                           _stream(x))
     _check(st, "w4a16_gemm")
+    return out
+
+
+def gemm_static(x, packed, scales, qzeros, group_size: int, out_dtype=None, out=None):
+    """:func:`gemm` through ``w4a16_gemm_static``: the library's split-K scratch comes from its
+    own static device array, so the call allocates nothing (``out`` is allocated here only
+    when not given). Calls that overlap on one GPU race on that array."""
+    M, K, N = _affine_operands(x, packed, scales, qzeros, group_size, None)
+    out = _out(out, M, N, out_dtype, x)
+    st = lib().w4a16_gemm_static(_ptr(x), M, K, N, _dt(x.dtype), _ptr(packed), _ptr(scales),
+                                 _ptr(qzeros), group_size, _ptr(out), _dt(out.dtype), _stream(x))
+    _check(st, "w4a16_gemm_static")
     return out
 
 

@@ -1,6 +1,8 @@
 // w4a16_api.hip - the C ABI declared in include/w4a16.h: host-side argument checks, then
 // dispatch on M to the decode or batched (tiled) kernels. Nothing is launched
 // unless every check passes; there is no fallback path.
+#include <mutex>
+
 #include "w4a16.h"
 #include "w4a16_launch.hpp"
 
@@ -81,6 +83,29 @@ w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
   return from_hip(w4a16::launch_decode(a));
 }
 
+// Scratch of w4a16_gemm_static: one file-scope device array per GPU (its split-K partial
+// tiles), of W4A16_STATIC_SCRATCH_BYTES. On the host, `scratch` names a host-side stand-in,
+// never the device memory: host code uses only the per-device address that
+// hipGetSymbolAddress returns, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[W4A16_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {nullptr};
+
+// the current device's copy of `scratch`, or nullptr if the lookup failed
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,6 +144,35 @@ w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
   a.group_size = group_size;
   a.out = out;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.stream = static_cast<hipStream_t>(stream);
+  return gemm_common(a, act, out_dtype);
+}
+
+w4a16_status w4a16_gemm_static(const void* x, int M, int K, int N, w4a16_dtype act,
+                               const int32_t* packed, const void* scales, const int32_t* qzeros,
+                               int group_size, void* out, w4a16_dtype out_dtype, void* stream) {
+  // the same checks as w4a16_gemm first; then the scratch this shape needs against the
+  // static maximum, before the device array is touched
+  if (M < 0) return W4A16_ERR_ARG;
+  const w4a16_status st = check_shape(K, N, group_size);
+  if (st != W4A16_OK) return st;
+  if (M == 0) return W4A16_OK;
+  const size_t need = workspace_need(M, K, N, group_size);
+  if (need > (size_t)W4A16_STATIC_SCRATCH_BYTES) return W4A16_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need) {
+    ws = device_scratch();
+    if (!ws) return W4A16_ERR_HIP;
+  }
+  GemmArgs a{};
+  a.x = x; a.M = M; a.K = K; a.N = N;
+  a.packed = reinterpret_cast<const uint32_t*>(packed);
+  a.scales = scales;
+  a.qzeros = reinterpret_cast<const uint32_t*>(qzeros);
+  a.codebook = nullptr; a.nf4 = false;
+  a.group_size = group_size;
+  a.out = out;
+  a.workspace = ws; a.workspace_bytes = need ? (size_t)W4A16_STATIC_SCRATCH_BYTES : 0;
   a.stream = static_cast<hipStream_t>(stream);
   return gemm_common(a, act, out_dtype);
 }
