@@ -89,7 +89,8 @@ def test_workspace_bytes(L):
     # 64 rows for the small tile, chosen when large tiles would not cover the chip)
     assert workspace_bytes(2048, 8192, 28672, 128) == 0
     assert workspace_bytes(200, 2048, 64, 128) == 8 * 256 * 64 * 4    # 8 slices of 2 k-blocks
-    assert workspace_bytes(32, 4096, 28672, 128) == 2 * 64 * 28672 * 4
+    assert workspace_bytes(48, 4096, 28672, 128) == 2 * 64 * 28672 * 4   # 2 slices
+    assert workspace_bytes(32, 4096, 28672, 128) == 0     # the skinny kernel reduces in LDS
 
 
 def test_awq_rejects_bad_s_inv_and_sizes_its_workspace(L):
@@ -108,7 +109,9 @@ def test_awq_rejects_bad_s_inv_and_sizes_its_workspace(L):
     assert awq_workspace_bytes(8, 14336, 4096, 128) == 8 * 14336 * 2
     assert awq_workspace_bytes(16, 14336, 4096, 128) == 16 * 14336 * 2
     assert awq_workspace_bytes(9, 9216, 256, 128) == 9 * 9216 * 2
-    assert awq_workspace_bytes(200, 2048, 64, 128) == workspace_bytes(200, 2048, 64, 128) > 0
+    # batched shapes: the activation tiles go to LDS untouched, so x' comes from a pre-pass
+    assert awq_workspace_bytes(200, 2048, 64, 128) == workspace_bytes(200, 2048, 64, 128) + 200 * 2048 * 2
+    assert awq_workspace_bytes(24, 4096, 14336, 128) == 24 * 4096 * 2   # skinny kernel: x' only
     assert awq_workspace_bytes(2048, 8192, 28672, 128) == 2048 * 8192 * 2   # 128x512 tile
     assert awq_workspace_bytes(129, 4224, 28688, 64) == \
         workspace_bytes(129, 4224, 28688, 64) + 129 * 4224 * 2                 # and K split
@@ -144,12 +147,20 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     assert kernel_name(16, 14336, 4096, 128).startswith("w4a16_decode")    # K N < 2^27
     assert kernel_name(16, 8192, 10240, 128).startswith("w4a16_decode")
     assert kernel_name(11, 8192, 57344, 128).startswith("w4a16_decode")    # fewer than 12 rows
-    assert kernel_name(12, 8192, 57344, 128).startswith("w4a16_tiled")
+    # x beyond the decode kernel's LDS: skinny up to 8192 deep, batched beyond
+    assert kernel_name(12, 8192, 57344, 128).startswith("w4a16_skinny")
     assert kernel_name(16, 28672, 8192, 128).startswith("w4a16_tiled")
     assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_decode")     # K N <= 2^24
     assert kernel_name(32, 4096, 4096, 128).startswith("w4a16_decode")
     assert kernel_name(33, 4096, 4096, 128).startswith("w4a16_tiled")
-    assert kernel_name(17, 4096, 6144, 128).startswith("w4a16_tiled")
+    # 17..32 rows: skinny where its 64-column tiles fill the chip (80 K/4096 <= N/64 <= 512)
+    assert kernel_name(17, 4096, 6144, 128).startswith("w4a16_skinny")
+    assert kernel_name(32, 4096, 28672, 128).startswith("w4a16_skinny")
+    assert kernel_name(24, 8192, 10240, 128).startswith("w4a16_skinny")
+    assert kernel_name(32, 8192, 8192, 128).startswith("w4a16_tiled")      # 128 tiles < 160
+    assert kernel_name(32, 8192, 57344, 128).startswith("w4a16_tiled")     # 896 tiles > 512
+    assert kernel_name(17, 14336, 4096, 128).startswith("w4a16_tiled")     # deeper than 8192
+    assert kernel_name(33, 4096, 14336, 128).startswith("w4a16_tiled")
 
 
 def test_nf4_requires_codebook(L):
@@ -183,7 +194,7 @@ def test_kernel_name_and_strings(L):
     assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_decode")     # K N <= 2^24
     assert kernel_name(32, 4096, 4096, 128).startswith("w4a16_decode")
     assert kernel_name(33, 4096, 4096, 128).startswith("w4a16_tiled")
-    assert kernel_name(17, 4096, 6144, 128).startswith("w4a16_tiled")
+    assert kernel_name(17, 4096, 6144, 128).startswith("w4a16_skinny")
     assert kernel_name(65, 4096, 4096, 128).startswith("w4a16_tiled")
     # the ragged full-size parity shapes land on each batched geometry (256 compute units)
     assert kernel_name(257, 2080, 44048, 32) == "w4a16_tiled_64x256"

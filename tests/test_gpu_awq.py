@@ -208,10 +208,12 @@ def test_awq_search_end_to_end(M, act, sym):
 
 def test_awq_graph_replays_match_eager():
     """Every AWQ path captured in one HIP graph (LDS prologue, persistent, workspace pre-pass
-    for decode and for the 128x512 tile, split K): replays equal the eager run bit for bit."""
+    for decode, for the skinny kernel and for the 128x512 tile, split K): replays equal the
+    eager run bit for bit."""
     import weight_only_int4_w4a16_amd as w4
     torch = torch_mod()
-    shapes = [(1, 1024, 512), (16, 2048, 28672), (12, 14336, 256), (130, 2048, 64), (1024, 2048, 16384)]
+    shapes = [(1, 1024, 512), (16, 2048, 28672), (12, 14336, 256), (130, 2048, 64), (1024, 2048, 16384),
+              (40, 2048, 4096)]
     calls, outs = [], []
     for i, (M, K, N) in enumerate(shapes):
         _announce(f"awq graph M={M} K={K} N={N} {_path(M, K, N, 128)}")

@@ -119,6 +119,15 @@ SMALL = [
     (256, 512, 256, 64, "f16", "nf4"),
     (300, 1024, 128, 128, "bf16", "sym"),
     (129, 2048, 32, 64, "bf16", "nf4"),
+    # skinny kernel (17..64 rows; K split across eight waves, reduced in LDS): uneven wave
+    # slices with idle waves (33 and 9 k-blocks), ragged K, a ragged last column tile (17 and
+    # 9 strips), one and two 32-row tiles, every format
+    (24, 4224, 4112, 32, "f16", "asym"),
+    (48, 1152, 272, 64, "f16", "nf4"),
+    (64, 2080, 144, 32, "bf16", "asym"),
+    (37, 640, 80, 64, "bf16", "sym"),
+    (61, 4096, 48, 128, "f16", "sym"),
+    (18, 2048, 8208, 128, "bf16", "nf4"),
 ]
 
 
@@ -157,6 +166,8 @@ SWIGLU = [
     (300, 1024, 544, 128, "f16", "asym"),    # batched 64x256, ragged tile
     (257, 2080, 2080, 32, "f16", "nf4"),
     (513, 2080, 16416, 32, "bf16", "asym"),  # batched 128x512
+    (48, 1024, 96, 64, "f16", "nf4"),        # skinny, two row tiles, ragged gate half
+    (33, 2176, 160, 128, "bf16", "sym"),     # skinny, ragged K
 ]
 
 
@@ -371,7 +382,8 @@ def test_graph_replays_match_eager():
     import weight_only_int4_w4a16_amd as w4
     torch = torch_mod()
     cases = [rtn_case(1, 1024, 256, 128, seed=11), rtn_case(4, 512, 128, 32, seed=12),
-             rtn_case(130, 2048, 64, 128, seed=13)]     # batched kernel, K split in two
+             rtn_case(130, 2048, 64, 128, seed=13),     # batched kernel, K split in two
+             rtn_case(40, 2048, 8208, 128, seed=14)]    # skinny kernel
     devs = [device_inputs(c) for c in cases]
     outs = [torch.empty((c["M"], c["N"]), dtype=torch.float16, device="cuda") for c in cases]
 

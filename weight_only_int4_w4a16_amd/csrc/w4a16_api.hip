@@ -1,6 +1,9 @@
 // w4a16_api.hip - the C ABI declared in include/w4a16.h: host-side argument checks, then
 // dispatch on M to the decode or batched (tiled) kernels. Nothing is launched
 // unless every check passes; there is no fallback path.
+#include <stdlib.h>
+#include <string.h>
+
 #include <mutex>
 
 #include "w4a16.h"
@@ -26,37 +29,72 @@ w4a16_status check_shape(int K, int N, int gs) {
 
 w4a16_status from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
-// M above 16 goes to the batched kernel: past one 16-row MFMA tile the decode kernel's
-// activation traffic per weight byte outgrows the batched kernel's dequantization cost
-// (4096x14336: M=32 takes 33.7 us on the decode kernel, M=64 24.8 us on the batched one)
-// The exception: from 12 rows on, a large weight (K N >= 2^27) whose x does not fit the decode
-// kernel's LDS staging (so every workgroup re-reads x from L2 with each group) runs faster on
-// the batched kernel (M=16: 8192x57344 118 -> 101 us, 28672x8192 58.7 -> 50.7 us; smaller
-// weights such as 8192x10240 and 14336x4096 stay faster on the decode kernel).
-// Small weights (K N <= 2^24) keep the decode kernel, in 16-row launches, up to 32 rows: their
-// batched tiles cannot fill the chip (4096x4096: M=17 15.8 -> 11.3 us, M=32 17.7 -> 14.5 us).
-bool use_tiled(const GemmArgs& a) {
-  if (!w4a16::tiled_supported(a)) return false;
-  if (a.M > 32) return true;
-  if (a.M > 16) return (long long)a.K * a.N > (1LL << 24);
-  if (a.M < 12 || (long long)a.K * a.N < (1LL << 27)) return false;
-  return !w4a16::decode_config(a.M, a.K, a.N, a.group_size, a.glu).x_in_lds;
+enum Path { PATH_DECODE = 0, PATH_SKINNY = 1, PATH_TILED = 2, PATH_AUTO = 3 };
+
+// W4A16_FORCE_KERNEL=decode|skinny|tiled pins the kernel for every shape (for benchmarking one
+// path against another); read once per process. Any other value, or none, leaves the choice
+// to the shape rules below.
+Path forced_path() {
+  static const Path forced = [] {
+    const char* v = getenv("W4A16_FORCE_KERNEL");
+    if (!v) return PATH_AUTO;
+    if (!strcmp(v, "decode")) return PATH_DECODE;
+    if (!strcmp(v, "skinny")) return PATH_SKINNY;
+    if (!strcmp(v, "tiled")) return PATH_TILED;
+    return PATH_AUTO;
+  }();
+  return forced;
+}
+
+// M <= 16 runs the decode kernel (one 16-row MFMA tile). 17..32 rows run the skinny kernel
+// (K split across the eight waves of a workgroup, reduced in LDS) on weights at most 8192 deep
+// with enough 64-column tiles to fill the chip (N/64 >= 80 K/4096) but not so many that the
+// batched kernel's larger tiles win (N/64 <= 512); measured at M=24/32, e.g. 4096x14336
+// 20.9 -> 16.5 / 21.6 -> 17.6 us, 8192x10240 27.4 -> 23.6 / 28.9 -> 27.0 us against the
+// batched kernel. Weights of at most 2^24 elements keep the decode kernel up to 32 rows, in
+// 16-row launches (their tiles cannot fill the chip otherwise: 4096x4096 at M=32 14.5 us). The
+// other shapes past 16 rows run the batched kernel (its 64x256 tiles with K split, or the
+// 128x512 tiles), e.g. 14336x4096 at M=32 23.1 us against 44.6 skinny. From 12 rows on, a large
+// weight (K N >= 2^27) whose x does not fit the decode kernel's LDS staging (so every decode
+// workgroup re-reads x from L2 with each group) leaves the decode kernel: for the skinny kernel
+// when at most 8192 deep (8192x57344 at M=12: 103.6 decode, 90.3 batched, 83.2 us skinny), for
+// the batched kernel otherwise (28672x8192 at M=12: 50.1 decode, 44.8 us batched).
+Path choose_path(const GemmArgs& a) {
+  const Path f = forced_path();
+  if (f != PATH_AUTO) return f;
+  const long long kn = (long long)a.K * a.N;
+  const int col_tiles = a.N / 64;
+  const bool skinny_fits = a.K <= 8192 && (long long)col_tiles * 4096 >= 80LL * a.K && col_tiles <= 512;
+  if (a.M > 32) return PATH_TILED;
+  if (a.M > 16) {
+    if (kn <= (1LL << 24)) return PATH_DECODE;
+    return skinny_fits ? PATH_SKINNY : PATH_TILED;
+  }
+  if (a.M < 12 || kn < (1LL << 27)) return PATH_DECODE;
+  if (w4a16::decode_config(a.M, a.K, a.N, a.group_size, a.glu).x_in_lds) return PATH_DECODE;
+  return a.K <= 8192 ? PATH_SKINNY : PATH_TILED;
 }
 
 size_t workspace_need(int M, int K, int N, int gs) {
   GemmArgs a{};
   a.M = M; a.K = K; a.N = N; a.group_size = gs;
-  if (use_tiled(a)) return w4a16::tiled_workspace_bytes(M, K, N);
-  return w4a16::decode_config(M < 16 ? M : 16, K, N, gs, false).workspace_bytes;
+  switch (choose_path(a)) {
+    case PATH_TILED: return w4a16::tiled_workspace_bytes(M, K, N);
+    case PATH_SKINNY: return 0;
+    default: return w4a16::decode_config(M < 16 ? M : 16, K, N, gs, false).workspace_bytes;
+  }
 }
 
-// AWQ-scaled x: decode launches whose x does not fit in LDS, and batched launches on the
-// large tile, scale it into the workspace first
+// AWQ-scaled x: decode launches whose x does not fit in LDS, skinny launches, and batched
+// launches on the large tile scale it into the workspace first
 size_t awq_workspace_need(int M, int K, int N, int gs) {
   GemmArgs a{};
   a.M = M; a.K = K; a.N = N; a.group_size = gs;
-  if (use_tiled(a)) return w4a16::tiled_awq_workspace_bytes(M, K, N);
-  return w4a16::decode_awq_workspace_bytes(M < 16 ? M : 16, K, N, gs);
+  switch (choose_path(a)) {
+    case PATH_TILED: return w4a16::tiled_awq_workspace_bytes(M, K, N);
+    case PATH_SKINNY: return w4a16::skinny_awq_workspace_bytes(M, K, N);
+    default: return w4a16::decode_awq_workspace_bytes(M < 16 ? M : 16, K, N, gs);
+  }
 }
 
 w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
@@ -79,8 +117,11 @@ w4a16_status gemm_common(GemmArgs& a, w4a16_dtype act, w4a16_dtype out_dtype) {
                                : workspace_need(a.M, a.K, a.N, a.group_size);
   if (need && (!a.workspace || !aligned(a.workspace, 256) || a.workspace_bytes < need))
     return W4A16_ERR_WORKSPACE;
-  if (use_tiled(a)) return from_hip(w4a16::launch_tiled(a));
-  return from_hip(w4a16::launch_decode(a));
+  switch (choose_path(a)) {
+    case PATH_TILED: return from_hip(w4a16::launch_tiled(a));
+    case PATH_SKINNY: return from_hip(w4a16::launch_skinny(a));
+    default: return from_hip(w4a16::launch_decode(a));
+  }
 }
 
 // Scratch of w4a16_gemm_static: one file-scope device array per GPU (its split-K partial
@@ -346,8 +387,11 @@ const char* w4a16_kernel_name(int M, int K, int N, int group_size) {
   if (M <= 0) return "none";
   GemmArgs a{};
   a.M = M; a.K = K; a.N = N; a.group_size = group_size;
-  if (use_tiled(a)) return w4a16::tiled_name(M, K, N);
-  return w4a16::decode_name(M, K, N, group_size, w4a16::ACT_F16);
+  switch (choose_path(a)) {
+    case PATH_TILED: return w4a16::tiled_name(M, K, N);
+    case PATH_SKINNY: return w4a16::skinny_name(M, K, N);
+    default: return w4a16::decode_name(M, K, N, group_size, w4a16::ACT_F16);
+  }
 }
 
 const char* w4a16_status_string(w4a16_status s) {

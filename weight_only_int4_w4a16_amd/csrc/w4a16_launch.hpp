@@ -53,7 +53,10 @@ hipError_t launch_pack(const uint32_t* qweight, int K, int N, uint32_t* packed, 
 hipError_t launch_dequant(const GemmArgs& a);  // writes W_hat [K][N] into a.out (act dtype)
 hipError_t launch_decode(const GemmArgs& a);   // M <= 16 (more rows: several launches)
 hipError_t launch_tiled(const GemmArgs& a);    // M > 16
-size_t tiled_workspace_bytes(int M, int K, int N);
+size_t tiled_workspace_bytes(int M, int K, int N);  // split-K partials (0 when K is not split)
+hipError_t launch_skinny(const GemmArgs& a);   // 17..64 rows: K split across the waves
+const char* skinny_name(int M, int K, int N);
+size_t skinny_awq_workspace_bytes(int M, int K, int N);
 size_t decode_awq_workspace_bytes(int M, int K, int N, int group_size);  // M <= 16
 size_t tiled_awq_workspace_bytes(int M, int K, int N);
 // W4A8: per-token INT8 quantization of x (xq [M][K], sx [M], and with perm the packed nibble

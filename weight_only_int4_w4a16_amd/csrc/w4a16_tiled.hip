@@ -23,7 +23,8 @@
 // contiguous slices, one workgroup each. Every slice stores its fp32 partial tile in the
 // workspace and a second small kernel sums the S partials in slice order (deterministic)
 // into the output.
-#include <type_traits>
+#include <stdlib.h>
+#include <string.h>
 
 #include "w4a16_device.hpp"
 #include "w4a16_launch.hpp"
@@ -32,25 +33,35 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kPairs = 2;           // 32-column strip pairs per wave (4 strips of 16)
-constexpr int kStrips = 2 * kPairs;
-constexpr int kAStride = 128 + 8;   // LDS row stride of the activation tile (halves)
 
-// Workgroup tile: MT 32-row MFMA tiles (kBM = 32 MT rows) by WAVES waves of 64 columns.
-// Large: 128 x 512, eight waves (two per SIMD). Small: 64 x 256, four waves, for GEMMs whose
-// large tiles would leave compute units idle (each large tile row of M <= 256 is 28-56
-// tiles at N = 14336).
-template <int MT, int WAVES>
+// Workgroup tile: MT 32-row MFMA tiles (kBM = 32 MT rows) by WAVES waves of NP 32-column
+// strip pairs. Large: 128 x 512, eight waves (two per SIMD) of two pairs. Small: 64 x 256, four
+// waves of two pairs, for GEMMs whose large tiles would leave compute units idle (each large
+// tile row of M <= 256 is 28-56 tiles at N = 14336).
+template <int MT, int WAVES, int NP, int STAGES>
 struct TileShape {
+  static constexpr int kStages = STAGES;  // blocks in flight: LDS slots and code register sets
   static constexpr int kMT = MT;
   static constexpr int kBM = 32 * MT;
+  static constexpr int kNP = NP;
+  static constexpr int kBN = 32 * NP * WAVES;
   static constexpr int kWaves = WAVES;
   static constexpr int kThreads = 64 * WAVES;
-  static constexpr int kAChunks = kBM * 16 / kThreads;  // 16-byte chunks per thread per block
-  static constexpr size_t kLdsBytes = 2 * kBM * kAStride * 2;  // double-buffered activations
+  static constexpr int kADma = kBM / 4 / WAVES;  // 1 KiB direct-to-LDS loads per wave per block
+  static constexpr size_t kSlotBytes = (size_t)kBM * 256;       // one activation tile
+  static constexpr size_t kLdsBytes = kStages * kSlotBytes;     // the ring of tiles
+  static_assert(kADma * WAVES * 4 == kBM, "the tile's rows split evenly over the waves");
 };
-typedef TileShape<4, 8> LargeTile;
-typedef TileShape<2, 4> SmallTile;
+// Stages: a small tile's block takes about one HBM round trip to multiply, so a workgroup that
+// streams many blocks loads three blocks ahead (4096x14336 at M=192/256, 32 blocks per
+// workgroup: 47.2 -> 43.7, 48.2 -> 45.4 us against one block ahead); with K split into short
+// slices (8 blocks) the deeper prologue costs more than it hides (5-10%), so those keep one
+// block ahead. The large tile's 128 accumulators leave registers for one block ahead, which
+// its four-times-longer blocks cover.
+typedef TileShape<4, 8, 2, 2> LargeTile;
+typedef TileShape<2, 4, 2, 2> SmallTile;
+typedef TileShape<2, 4, 2, 4> SmallTileDeep;
+constexpr int kDeepBlocks = 16;  // k-blocks per workgroup from which the small tile goes deep
 
 enum Fmt { FMT_ASYM = 0, FMT_SYM = 1, FMT_NF4 = 2 };
 
@@ -75,7 +86,6 @@ struct TiledParams {
   int S, kps;          // K slices and k-blocks per slice
   float* partials;     // [S][tiles_m * tile rows][N] fp32 (S > 1)
   int half;            // GLU: strips per half of the fused gate+up weight (NT / 2)
-  const uint16_t* xscale;  // XS: AWQ S^-1 [K] in the activation type
 };
 
 // workgroup -> output tile, so that tiles sharing weight columns run on the same XCD
@@ -84,19 +94,51 @@ __device__ __forceinline__ int tile_of(int b, int G) {
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
+// s_waitcnt with only the vector-memory counter bounded: vmcnt <= n, the LDS and export
+// counters left alone (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8). The
+// counter holds at most 63 (a wave stalls at issue beyond that), so larger n wait for 63: a
+// stricter, still correct condition.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0, "a count of outstanding instructions");
+  constexpr int c = n < 63 ? n : 63;
+  __builtin_amdgcn_s_waitcnt((c & 0xF) | ((c >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Sixteen zero bytes in device memory: the source of the activation chunks past a ragged K.
+__device__ __attribute__((aligned(16))) const uint16_t kZeroChunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes dst + 16 l (dst is
+// the same for the whole wave)
+__device__ __forceinline__ void copy16_to_lds(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
 // GLU: the weight is a fused gate+up projection [K][2 Nh] (gate columns first). A wave's
 // first strip pair is two gate strips, its second the matching up strips, and the output is
 // h = SiLU(gate) * up, [M][Nh] (with K split, both halves go to the partials and the GLU
 // reduce kernel forms h).
-// XS: AWQ input scaling, x' = RN(x * s_inv[k]) as the activation tile goes to LDS.
-template <int ACT, int GPC, int FMT, class T, bool GLU, bool XS>
+//
+// Pipeline. The activation tile of a k-block (kBM rows x 128 k) goes from HBM straight to LDS
+// (global_load_lds_dwordx4: no registers, no LDS stores, no masking instructions) into one of
+// two slots, and the codes, scales and zero-points of the block into one of two register
+// sets, one block ahead of the MFMAs. Row r of a slot holds its sixteen 16-byte k-chunks at
+// positions c ^ (r % 16), so the A-fragment reads of sixteen consecutive rows fall in sixteen
+// different bank groups. Each wave waits for its own copies of the block (vmcnt: only that
+// block's code and metadata loads were issued after them) and a barrier makes every wave's
+// copies visible; the same barrier frees the other slot, into which the next block loads.
+template <int ACT, int GPC, int FMT, class T, bool GLU>
 __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
-  constexpr int kMT = T::kMT, kBM = T::kBM, kWaves = T::kWaves, kThreads = T::kThreads;
-  constexpr int kAChunks = T::kAChunks;
+  constexpr int kMT = T::kMT, kBM = T::kBM, kWaves = T::kWaves, kADma = T::kADma;
+  constexpr int kPairs = T::kNP, kStrips = 2 * T::kNP, kStages = T::kStages;
+  static_assert(!GLU || kPairs == 2, "a SwiGLU wave holds a gate pair and an up pair");
   typedef typename ActT<ACT>::type AT;
-  constexpr int SPG = 4 / GPC;
   constexpr bool ZEROS = FMT == FMT_ASYM;
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds_a[];  // [2][kBM * kAStride]
+  // vector-memory instructions one wave issues per block after its activation copies: two
+  // code chunks per pair, and per pair and scale group a scale (and a zero word); and in all
+  constexpr int kLoadsAfterCopies = kPairs * 2 + kPairs * GPC * (ZEROS ? 2 : 1);
+  constexpr int kLoadsPerBlock = kADma + kLoadsAfterCopies;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_a[];  // [kStages][kBM][128]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -116,30 +158,31 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   };
   const int shift = 4 * (lane & 7);
 
-  // ---- one k-block of operands: the activation tile slice this thread copies to LDS, and
-  // the codes + metadata of this wave's strips (kept in registers until the MFMAs) ----
+  // this lane's part of the activation copies: instruction j of the wave covers tile rows
+  // 4 (wave kADma + j) .. +3, lane l row + l/16 and slot position l%16, which holds k-chunk
+  // (l%16) ^ (row % 16) of that row (rows past M repeat row M-1 and are never stored; chunks
+  // past a ragged K are copied from a zero chunk, so they add nothing to the sums)
+  const uint16_t* arow[kADma];
+  int achunk[kADma];
+#pragma unroll
+  for (int j = 0; j < kADma; ++j) {
+    const int row = 4 * (wave * kADma + j) + (lane >> 4);
+    achunk[j] = ((lane & 15) ^ (row & 15)) * 8;
+    arow[j] = p.x + (size_t)min(m0 + row, M - 1) * K;
+  }
+  auto copy_a = [&](int kc, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kADma; ++j)
+      copy16_to_lds(kc * 128 + achunk[j] < K ? arow[j] + kc * 128 + achunk[j] : kZeroChunk,
+                    lds_a + (size_t)slot * kBM * 128 + (size_t)(wave * kADma + j) * 512);
+  };
+
   struct Regs {
-    int kc;
-    u4_t a[kAChunks];
-    u4_t xsc;                  // XS: s_inv for this thread's k chunk (the same in every row)
     u4_t b[kPairs][2];         // chunks 16h + c and 32 + 16h + c (h = lane/32, c = lane%16)
     uint32_t s[kPairs][GPC];   // 16-bit scale zero-extended by the load itself
     uint32_t z[kPairs][GPC];
   };
-  auto load = [&](Regs& R, int kc) {
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int row = c >> 4, kch = c & 15;
-      const int gm = min(m0 + row, M - 1);
-      const int k = kc * 128 + kch * 8;
-      // a ragged K ends inside the last block: load an in-bounds chunk (zeroed in store_a)
-      R.a[i] = *reinterpret_cast<const u4_t*>(p.x + (size_t)gm * K + min(k, K - 8));
-    }
-    static_assert(kThreads % 16 == 0, "a thread's k chunk is threadIdx.x % 16 in every row");
-    if constexpr (XS)
-      R.xsc = *reinterpret_cast<const u4_t*>(p.xscale + min(kc * 128 + (int)(threadIdx.x & 15) * 8, K - 8));
-    R.kc = kc;
+  auto load_b = [&](Regs& R, int kc) __attribute__((always_inline)) {
 #pragma unroll
     for (int pr = 0; pr < kPairs; ++pr) {
       // strips past N: loaded in bounds, never stored
@@ -157,17 +200,11 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
       }
     }
   };
-  auto store_a = [&](const Regs& R, int buf) {
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int row = c >> 4, kch = c & 15;
-      const bool in_k = R.kc * 128 + kch * 8 < K;
-      u4_t v = R.a[i];
-      if constexpr (XS) v = scale_act8<ACT>(v, R.xsc);
-      *reinterpret_cast<u4_t*>(lds_a + buf * kBM * kAStride + row * kAStride + kch * 8) =
-          in_k ? v : u4_t{0u, 0u, 0u, 0u};
-    }
+  // one block's loads, in a fixed order (activation copies first)
+  auto load = [&](Regs& R, int kc, int slot) __attribute__((always_inline)) {
+    copy_a(kc, slot);
+    load_b(R, kc);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   Nf4Lut lut;
@@ -181,64 +218,103 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][pr][i] = 0.f;
 
-  auto compute = [&](const Regs& R, int buf) {
-    const uint16_t* as = lds_a + buf * kBM * kAStride;
+  // One 16-k step's operands: the B fragments of both pairs, dequantized in registers, and
+  // the A fragments of the kMT row tiles, read from a slot.
+  auto dequant_step = [&](const Regs& R, int t, AT (&bf)[kPairs]) __attribute__((always_inline)) {
+    const int gi = t / (8 / GPC);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {  // 16-k steps of the block
-      const int gi = t / (8 / GPC);
-      AT bf[kPairs];
+    for (int pr = 0; pr < kPairs; ++pr) {
+      const uint32_t w = R.b[pr][t & 1][t >> 1];
+      const uint32_t sraw = R.s[pr][gi];
+      if constexpr (FMT == FMT_NF4) {
+        if constexpr (ACT == ACT_F16)
+          bf[pr] = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
+        else
+          bf[pr] = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
+      } else {
+        const uint32_t zq = ZEROS ? (R.z[pr][gi] >> shift) & 0xFu : 8u;
+        if constexpr (ACT == ACT_F16)
+          bf[pr] = dequant_word_f16(w, make_zero_f16(zq), as_h2(sraw * 0x00010001u));
+        else
+          bf[pr] = dequant_word_bf16(w, make_zero_f32(zq, __builtin_bit_cast(float, sraw << 16)));
+      }
+    }
+  };
+  auto read_a = [&](int slot, int t, u4_t (&a)[kMT]) __attribute__((always_inline)) {
+    const uint16_t* as = lds_a + (size_t)slot * kBM * 128;
 #pragma unroll
-      for (int pr = 0; pr < kPairs; ++pr) {
-        const uint32_t w = R.b[pr][t & 1][t >> 1];
-        const uint32_t sraw = R.s[pr][gi];
-        if constexpr (FMT == FMT_NF4) {
-          if constexpr (ACT == ACT_F16)
-            bf[pr] = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
-          else
-            bf[pr] = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
-        } else {
-          const uint32_t zq = ZEROS ? (R.z[pr][gi] >> shift) & 0xFu : 8u;
-          if constexpr (ACT == ACT_F16)
-            bf[pr] = dequant_word_f16(w, make_zero_f16(zq), as_h2(sraw * 0x00010001u));
-          else
-            bf[pr] = dequant_word_bf16(w, make_zero_f32(zq, __builtin_bit_cast(float, sraw << 16)));
-        }
+    for (int mt = 0; mt < kMT; ++mt) {  // row 32 mt + l%32, k-chunk 2 t + l/32 of the block
+      const int row = mt * 32 + (lane & 31);
+      const int c = (2 * t + (lane >> 5)) ^ (row & 15);
+      a[mt] = *reinterpret_cast<const u4_t*>(as + row * 128 + c * 8);
+    }
+  };
+
+  // Software pipeline over the 8 steps of a block: step t+1's A fragments are read (small
+  // tile; the large tile's 128 accumulators leave no room for a second set, so there each is
+  // read right before its MFMAs) and its B fragments dequantized while step t's MFMAs run.
+  constexpr bool PREFETCH_A = kMT <= 2;
+  auto compute = [&](const Regs& R, int slot) __attribute__((always_inline)) {
+    u4_t a[kMT];
+    AT bf[kPairs];
+    read_a(slot, 0, a);
+    dequant_step(R, 0, bf);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      u4_t an[kMT];
+      AT bn[kPairs];
+      if (t < 7) {
+        if constexpr (PREFETCH_A) read_a(slot, t + 1, an);
+        dequant_step(R, t + 1, bn);
+      }
+      if constexpr (!PREFETCH_A) {
+        if (t > 0) read_a(slot, t, a);
       }
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        // A: row 32 mt + l%32, k = 16 t + 8 (l/32) .. +8
-        const u4_t a = *reinterpret_cast<const u4_t*>(
-            as + (mt * 32 + (lane & 31)) * kAStride + t * 16 + (lane >> 5) * 8);
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int pr = 0; pr < kPairs; ++pr)
-          acc[mt][pr] = mfma32(__builtin_bit_cast(AT, a), bf[pr], acc[mt][pr]);
+          acc[mt][pr] = mfma32(__builtin_bit_cast(AT, a[mt]), bf[pr], acc[mt][pr]);
+      if (t < 7) {
+        if constexpr (PREFETCH_A) {
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt) a[mt] = an[mt];
+        }
+#pragma unroll
+        for (int pr = 0; pr < kPairs; ++pr) bf[pr] = bn[pr];
       }
     }
   };
 
-  // Two register sets and two LDS buffers: block i+1 loads while block i is multiplied.
-  // Loads are unconditional (past the slice they re-read its last block, never used), so
-  // the in-order load counter only ever waits for the set about to be used; a scheduling
-  // barrier after each batch of loads keeps the compiler from sinking them below the MFMAs.
+  // Block i is multiplied from slot i % kStages and register set i % kStages while blocks
+  // i+1 .. i+kStages-1 load. Loads are unconditional (past the slice they re-read its last
+  // block, never used), so every wave issues the same vector-memory instructions per block
+  // and the wait count is exact: after block i's copies come its own code loads and the
+  // kStages-2 later blocks' loads.
   const int nb = kc1 - kc0;
-  Regs R0, R1;
-  load(R0, kc0);
-  store_a(R0, 0);
-  __syncthreads();
+  const int kl = kc1 - 1;
+  Regs R[kStages];
+#pragma unroll
+  for (int st = 0; st + 1 < kStages; ++st) load(R[st], min(kc0 + st, kl), st);
+  auto step_block = [&](const Regs& Rb, Regs& Rfree, int i, int slot) __attribute__((always_inline)) {
+    wait_vmcnt<kLoadsAfterCopies + (kStages - 2) * kLoadsPerBlock>();  // block i's copies landed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no LDS access moves across the barrier
+    __builtin_amdgcn_s_barrier();             // every wave's copies of block i are in LDS, and
+                                              // every wave is done with block i-1's slot
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    load(Rfree, min(kc0 + i + kStages - 1, kl), (slot + kStages - 1) % kStages);
+    compute(Rb, slot);
+  };
   int i = 0;
-  for (; i + 1 < nb; i += 2) {
-    load(R1, kc0 + i + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(R0, 0);
-    store_a(R1, 1);
-    __syncthreads();
-    load(R0, min(kc0 + i + 2, kc1 - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(R1, 1);
-    store_a(R0, 0);
-    __syncthreads();
+  for (; i + kStages - 1 < nb; i += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) step_block(R[u], R[(u + kStages - 1) % kStages], i + u, u);
   }
-  if (i < nb) compute(R0, 0);
+#pragma unroll
+  for (int u = 0; u + 1 < kStages; ++u)
+    if (i + u < nb) step_block(R[u], R[(u + kStages - 1) % kStages], i + u, u);
+  // the loads still in flight (re-reads past the slice) retire before the wave ends
 
   // ---- epilogue ----
   // lane l holds column 32*pair + l%32 and rows 32*mt + 8*(i/4) + 4*(l/32) + i%4, i < 16
@@ -332,20 +408,22 @@ int cu_count_tiled() {
   return v;
 }
 
+enum TileKind { TILE_LARGE = 0, TILE_SMALL = 1 };
+
 struct TiledGeometry {
-  bool small;          // SmallTile instead of LargeTile
+  int kind;            // TileKind
   int bm, bn;          // tile rows and columns
   int tiles_m, tiles_n, S, kps;
   size_t partial_bytes;
 };
 
 // A tile kind with K cut into (about) S contiguous slices of whole k-blocks.
-TiledGeometry geometry_for(int M, int K, int N, bool small, int S) {
+TiledGeometry geometry_for(int M, int K, int N, int kind, int S) {
   TiledGeometry g;
   const int KC = ceil_div(K, 128);
-  g.small = small;
-  g.bm = small ? SmallTile::kBM : LargeTile::kBM;
-  g.bn = 16 * kStrips * (small ? SmallTile::kWaves : LargeTile::kWaves);
+  g.kind = kind;
+  g.bm = kind == TILE_LARGE ? LargeTile::kBM : SmallTile::kBM;
+  g.bn = kind == TILE_LARGE ? LargeTile::kBN : SmallTile::kBN;
   g.tiles_m = ceil_div(M, g.bm);
   g.tiles_n = ceil_div(N, g.bn);
   g.kps = ceil_div(KC, S);
@@ -364,14 +442,27 @@ double modelled_us(const TiledGeometry& g, int M, int N, int cus) {
   const long wgs = (long)g.tiles_m * g.tiles_n * g.S;
   const long per_cu = (wgs + cus - 1) / cus;
   const double wg_flops = 2.0 * g.bm * g.bn * g.kps * 128;
-  const double rate = !g.small ? 4.6e6 : per_cu > 1 ? 3.4e6 : 2.7e6;  // flop per us
+  const double rate = g.kind == TILE_LARGE ? 4.6e6 : per_cu > 1 ? 3.4e6 : 2.7e6;  // flop per us
   double us = per_cu * (2.5 + wg_flops / rate);
   if (g.S > 1) us += 2.0 * g.S * M * (double)N * 4 / 5e6 + 2.0;
   return us;
 }
 
-// Tile and K split: the large tile (each dequantized word feeds four 32-row tiles, not two)
-// or the small one (more workgroups), each with S = 1, 2, 4, ... slices of at least two
+// W4A16_FORCE_TILE=large|small pins the batched kernel's tile kind (its K split is still
+// chosen by the model), for benchmarking one tile against another; read once per process.
+int forced_tile() {
+  static const int forced = [] {
+    const char* v = getenv("W4A16_FORCE_TILE");
+    if (!v) return -1;
+    if (!strcmp(v, "large")) return (int)TILE_LARGE;
+    if (!strcmp(v, "small")) return (int)TILE_SMALL;
+    return -1;
+  }();
+  return forced;
+}
+
+// Tile and K split: the large tile (each dequantized word feeds four 32-row tiles) or the small
+// one (more workgroups), each with S = 1, 2, 4, ... slices of at least two
 // k-blocks and at most four workgroups per compute unit; the model's fastest wins. It
 // tracks the measured choices: large wins by 12-21% at 8192x28672 M=256, 28672x8192 M=256,
 // 8192x10240 M=512 and loses by 7-13% at 4096x4096 M=512 and 1024 (split-K partials
@@ -379,53 +470,43 @@ double modelled_us(const TiledGeometry& g, int M, int N, int cus) {
 TiledGeometry tiled_geometry(int M, int K, int N) {
   const int cus = cu_count_tiled();
   const int KC = ceil_div(K, 128);
-  TiledGeometry best = geometry_for(M, K, N, true, 1);
-  double best_us = modelled_us(best, M, N, cus);
-  for (int small = 0; small < 2; ++small)
+  const int f = forced_tile();
+  TiledGeometry best{};
+  double best_us = -1;
+  for (int kind = 0; kind < 2; ++kind) {
+    if (f >= 0 && kind != f) continue;
     for (int S = 1; S == 1 || KC / S >= 2; S *= 2) {
-      const TiledGeometry g = geometry_for(M, K, N, small != 0, S);
+      const TiledGeometry g = geometry_for(M, K, N, kind, S);
       if (S > 1 && (long)g.tiles_m * g.tiles_n * g.S > 4L * cus) break;
       const double us = modelled_us(g, M, N, cus);
-      if (us < best_us) {
+      if (best_us < 0 || us < best_us) {
         best = g;
         best_us = us;
       }
     }
+  }
   return best;
 }
 
 template <int ACT, int GPC, class T, bool GLU>
 hipError_t launch_glu(const GemmArgs& a, const TiledParams& p, dim3 grid) {
   if (a.nf4)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4, T, GLU, false>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   else if (a.qzeros)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, GLU, false>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   else
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T, GLU, false>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   return hipGetLastError();
-}
-
-// AWQ-scaled activations, small tile: the plain GEMM, affine formats, x scaled as it is
-// staged (the large tile takes x' from a pre-pass instead: the multiply there cost 8% of the
-// bf16 prefill GEMM against 1-2% for the pre-pass)
-template <int ACT, int GPC, class T>
-hipError_t launch_xs(const GemmArgs& a, const TiledParams& p, dim3 grid) {
-  if constexpr (!std::is_same<T, SmallTile>::value) {
-    return hipErrorNotSupported;
-  } else {
-    if (a.nf4 || a.glu) return hipErrorNotSupported;
-    if (a.qzeros)
-      hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, false, true>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
-    else
-      hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_SYM, T, false, true>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
-    return hipGetLastError();
-  }
 }
 
 template <int ACT, int GPC, class T>
 hipError_t launch_fmt(const GemmArgs& a, const TiledParams& p, dim3 grid) {
-  if (p.xscale) return launch_xs<ACT, GPC, T>(a, p, grid);
-  return a.glu ? launch_glu<ACT, GPC, T, true>(a, p, grid) : launch_glu<ACT, GPC, T, false>(a, p, grid);
+  if constexpr (T::kNP == 2) {
+    if (a.glu) return launch_glu<ACT, GPC, T, true>(a, p, grid);
+  } else {
+    if (a.glu) return hipErrorNotSupported;  // the launcher never sends a SwiGLU call here
+  }
+  return launch_glu<ACT, GPC, T, false>(a, p, grid);
 }
 
 template <int ACT, class T>
@@ -448,14 +529,15 @@ bool tiled_supported(const GemmArgs&) { return true; }
 
 const char* tiled_name(int M, int K, int N) {
   const TiledGeometry g = tiled_geometry(M, K, N);
-  if (g.small) return g.S > 1 ? "w4a16_tiled_64x256_splitk" : "w4a16_tiled_64x256";
+  if (g.kind == TILE_SMALL) return g.S > 1 ? "w4a16_tiled_64x256_splitk" : "w4a16_tiled_64x256";
   return g.S > 1 ? "w4a16_tiled_128x512_splitk" : "w4a16_tiled_128x512";
 }
 
-// AWQ: the large tile reads x' from a pre-pass, placed after the split-K partials
+// AWQ: the activation tiles go from HBM to LDS untouched, so the kernel reads x' from a
+// pre-pass, placed after the split-K partials
 size_t tiled_awq_workspace_bytes(int M, int K, int N) {
   const TiledGeometry g = tiled_geometry(M, K, N);
-  return g.small ? g.partial_bytes : align256(g.partial_bytes) + align256((size_t)M * K * 2);
+  return align256(g.partial_bytes) + align256((size_t)M * K * 2);
 }
 
 size_t tiled_workspace_bytes(int M, int K, int N) {
@@ -485,16 +567,16 @@ hipError_t launch_tiled(const GemmArgs& a) {
   p.kps = g.kps;
   p.partials = g.S > 1 ? static_cast<float*>(a.workspace) : nullptr;
   p.half = p.NT / 2;
-  p.xscale = static_cast<const uint16_t*>(a.xscale);
-  if (a.xscale && !g.small) {
+  if (a.xscale) {
     void* xs = static_cast<char*>(a.workspace) + align256(g.partial_bytes);
     const hipError_t e = launch_awq_scale(a.x, a.xscale, a.M, a.K, a.act, xs, a.stream);
     if (e != hipSuccess) return e;
     p.x = static_cast<const uint16_t*>(xs);
-    p.xscale = nullptr;
   }
   const dim3 grid(g.tiles_m * g.tiles_n, g.S);
-  const hipError_t e = g.small ? launch_act<SmallTile>(a, p, grid) : launch_act<LargeTile>(a, p, grid);
+  const hipError_t e = g.kind == TILE_LARGE      ? launch_act<LargeTile>(a, p, grid)
+                       : g.kps >= kDeepBlocks      ? launch_act<SmallTileDeep>(a, p, grid)
+                                                   : launch_act<SmallTile>(a, p, grid);
   if (e != hipSuccess || g.S == 1) return e;
   const size_t slice_stride = (size_t)g.tiles_m * g.bm * a.N;
   if (a.glu) {
