@@ -84,6 +84,7 @@ SMALL = [
     (70, 256, 32, 64, "f16", "nf4"),
     # decode launches with activations too large for LDS (16 rows of 8192 k: 256 KiB)
     (16, 8192, 32, 128, "f16", "asym"),
+    (16, 8192, 64, 64, "f16", "nf4"),       # fp16 NF4 levels gathered per word (no nibble-order x)
     (9, 4224, 48, 64, "bf16", "sym"),
     (16, 8320, 32, 32, "f16", "asym"),
     (16, 1024, 48, 64, "bf16", "asym"),
@@ -160,6 +161,7 @@ SWIGLU = [
     (12, 4096, 16416, 128, "f16", "asym"),   # persistent, one group per wave
     (9, 4224, 16448, 64, "bf16", "nf4"),     # persistent, several groups per wave
     (2, 1024, 96, 64, "bf16", "nf4"),
+    (4, 1024, 96, 64, "f16", "nf4"),         # fp16 NF4, x in LDS in nibble order, SwiGLU tile
     (17, 512, 64, 128, "bf16", "asym"),      # decode, two launches (16 + 1 rows)
     (20, 4096, 4128, 128, "bf16", "asym"),   # batched 64x256, K split
     (130, 2144, 96, 32, "f16", "sym"),
@@ -311,6 +313,28 @@ def test_repeat_runs_are_bit_identical():
     a = from_dev(run_gemm(c, d, out_dtype=torch.float32))
     b = from_dev(run_gemm(c, d, out_dtype=torch.float32))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K,N,g", [(1, 28672, 512, 128), (4, 28672, 256, 128), (16, 14336, 256, 32)])
+def test_large_activation_channels(M, K, N, g):
+    """"4.3 Weight-only INT4", section 3.1: a few input channels carry activations far above the
+    rest. One channel in 32 is scaled by 10..100 (so |x| reaches several hundred) on the fp16
+    decode path, which multiplies the exact integers 1024 + q and -(1024 + z) and cancels them
+    in fp32 sums before each group's scale (about ten bits of the 24 cancel): every output stays
+    within the 1e-3 max|y_ref| bound of the fp64 oracle."""
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    _announce(f"large channels M={M} K={K} N={N} g={g} kernel={w4.kernel_name(M, K, N, g)}")
+    c = rtn_case(M, K, N, g, "f16", seed=K + N + M)
+    x = c["x"].astype(np.float64)
+    ch = np.arange(7, K, 32)
+    x[:, ch] *= np.linspace(10.0, 100.0, len(ch))[None, :]
+    c["x"] = x.astype(np.float16)
+    assert np.max(np.abs(c["x"].astype(np.float64))) > 200
+    d = device_inputs(c)
+    y_ref = oracle.gemm_ref(c["x"], c["w_hat"])
+    y = from_dev(run_gemm(c, d, out_dtype=torch.float32)).astype(np.float64)
+    assert_close(y, y_ref, "fp32 out, outlier channels")
 
 
 # ------------------------------------------------------------------ the single-GEMV workload

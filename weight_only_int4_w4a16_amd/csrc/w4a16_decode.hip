@@ -1,5 +1,8 @@
 // w4a16_decode.hip - host side of the decode kernel (w4a16_decode_kernel.hpp): launch
 // geometry and dispatch on activation type and weight format.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "w4a16_decode_kernel.hpp"
 
 namespace w4a16 {
@@ -60,8 +63,24 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
 // loads are in flight while the wave partials are summed), the launch one more. Measured:
 // 4096x28672 at M=16 33.5 -> 23.0 us, 8192x57344 at M=8 77.9 -> 54.7 us, 8192x10240 at M=8
 // 21.0 -> 18.2 us; at M=4 the same rule would lose (4096x28672 17.3 -> 20.4 us).
-DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu) {
+// W4A16_DECODE_GEOMETRY=SW,W limits the choice below to tiles of SW strips and W waves per
+// workgroup where such a launch exists (for benchmarking geometries against each other); read
+// once per process.
+struct ForcedGeometry { int sw, w; };
+ForcedGeometry forced_geometry() {
+  static const ForcedGeometry f = [] {
+    ForcedGeometry r{0, 0};
+    const char* v = getenv("W4A16_DECODE_GEOMETRY");
+    if (v && sscanf(v, "%d,%d", &r.sw, &r.w) != 2) r = ForcedGeometry{0, 0};
+    return r;
+  }();
+  return f;
+}
+
+DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu,
+                    bool allow_forced = true) {
   const int KC = ceil_div(K, 128), NT = N / 16;
+  const ForcedGeometry fg = allow_forced ? forced_geometry() : ForcedGeometry{0, 0};
   const int rows = M < 16 ? M : 16, MT = ceil_div(rows, 16);
   const int GPC = 128 / group_size;
   const int cus = cu_count();
@@ -73,8 +92,10 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu
     if (NT % SW) continue;
     if (SW > 1 && !glu && !(x_in_lds && MT == 1 && GPC == 1)) continue;
     const int D = decode_group_blocks(SW, GPC, x_in_lds);  // k-blocks per pipeline group
+    if (fg.sw && fg.sw != SW) continue;
     for (int W = wmax; W >= 1; W >>= 1) {
       if (W > 1 && W > KC / D) continue;  // every wave streams at least one whole group
+      if (fg.w && fg.w != W) continue;
       DecodeConfig c = geometry(M, K, N, x_in_lds, SW, W);
       // the same number of groups per wave with whole groups only, on fewer waves where the
       // slice would end in a partial group (14336 = 112 blocks: 14 waves of 8, not 16 of 7;
@@ -116,17 +137,23 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu
       }
     }
   }
+  if (fg.sw) {  // a forced geometry as it is, or the unforced choice if it does not exist
+    return best_cost >= 0 ? best : choose(M, K, N, group_size, x_in_lds, glu, false);
+  }
   if (rows >= 8 && best_rounds > 1 && pbest_cost >= 0) return pbest;
-  // One row of x, and a wave that would stream more than 8 groups one after another: twice the
-  // waves on half the slice each, when every workgroup still fits at once. The model above
-  // counts 16 resident waves per compute unit; these 60-register instantiations fit 32, and
-  // with x this small LDS does not limit them (8192x57344: 2 -> 4 waves, 47 -> 44 us).
-  if (rows == 1 && x_in_lds && best.W * 2 <= wmax) {
+  // One row of x: the waves of a tile stream four groups each where the tile allows it. The
+  // model above counts launch rounds, but a wave keeps only two groups in flight, so shorter,
+  // more numerous waves keep more loads outstanding, and below four groups a wave's prologue
+  // (staging its slice of x) and epilogue are no longer amortized. Measured at M=1
+  // (8192x57344: 16, 8, 4, 2 groups per wave 46.4, 43.1, 40.6, 51.6 us; the other benchmarked
+  // shapes already stream four to eight groups per wave at their best geometry).
+  if (rows == 1 && x_in_lds) {
     const int D = decode_group_blocks(best.SW, GPC, x_in_lds);
-    if (ceil_div(best.slice, D) > 8) {
+    while (best.W * 2 <= wmax && ceil_div(ceil_div(KC, best.W * 2), D) >= 4) {
       DecodeConfig c = geometry(M, K, N, x_in_lds, best.SW, best.W * 2);
       c.glu = glu;
-      if (c.lds_bytes * (32 / c.W) <= kMaxLds && c.tiles <= (long)cus * (32 / c.W)) return c;
+      if (c.lds_bytes > kMaxLds) break;
+      best = c;
     }
   }
   return best;
