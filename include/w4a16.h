@@ -234,6 +234,16 @@ const char* w4a16_kernel_name(int M, int K, int N, int group_size);
 /* Static description of a status code. */
 const char* w4a16_status_string(w4a16_status status);
 
+/* Measurement hook, not part of the GEMM path: the device's practical HBM read ceiling, for
+ * reporting beside the published peak. Reads every 16-byte chunk of buf[0, bytes) once, each
+ * wave streaming a contiguous run with the 16-byte non-temporal loads the GEMM kernels use for
+ * the packed codes, and XORs folds of the words into the sink words (so no load is dead code):
+ * afterwards the XOR of the 256 sink words has changed by the XOR of all words of buf.
+ *   buf   [in]     device buffer, 16-byte aligned; bytes a multiple of 16 (0: no-op)
+ *   sink  [in/out] 256 device uint32 words, 4-byte aligned
+ * Bad arguments return W4A16_ERR_ARG before anything is launched. */
+w4a16_status w4a16_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Library version string. */
 const char* w4a16_version(void);
 

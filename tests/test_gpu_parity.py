@@ -435,3 +435,19 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert np.array_equal(from_dev(o).view(np.uint16), e.view(np.uint16)), f"replay {r}"
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 1 << 20, (3 << 20) + 16 * 7])
+def test_read_probe_reads_every_chunk_once(nbytes):
+    """The streaming-read probe (the bandwidth ceiling reported by the benchmark): the XOR of
+    its sink words is the XOR of every 32-bit word of the buffer, so a chunk read twice
+    (cancelled) or skipped changes it."""
+    import weight_only_int4_w4a16_amd as w4
+    torch = torch_mod()
+    words = np.random.default_rng(nbytes).integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    w4.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    folded = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert int(folded) == int(np.bitwise_xor.reduce(words))

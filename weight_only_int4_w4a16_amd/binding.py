@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_kernel_name.restype = ctypes.c_char_p
     L.w4a16_status_string.argtypes = [i32]
     L.w4a16_status_string.restype = ctypes.c_char_p
+    L.w4a16_read_probe.argtypes = [vp, sz, vp, vp]
+    L.w4a16_read_probe.restype = i32
     L.w4a16_version.argtypes = []
     L.w4a16_version.restype = ctypes.c_char_p
     _lib = L
@@ -446,6 +448,18 @@ def dequant_nf4(packed, absmax, codebook, K: int, block_size: int = 64, wdtype=N
                                  _dt(wdtype), _ptr(w), _stream(absmax))
     _check(st, "w4a16_dequant_nf4")
     return w
+
+
+def read_probe(buf, sink):
+    """Measurement hook: stream every byte of the contiguous device tensor ``buf`` once (its
+    size a multiple of 16 bytes), XOR-folding the words into ``sink`` (a contiguous 256-element
+    int32/uint32 device tensor); for timing the device's practical HBM read rate."""
+    if not buf.is_contiguous() or not sink.is_contiguous() or sink.numel() != 256 \
+            or sink.element_size() != 4:
+        _fail("buf must be contiguous and sink 256 contiguous 32-bit elements")
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().w4a16_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(buf))
+    _check(st, "w4a16_read_probe")
 
 
 def kernel_name(M: int, K: int, N: int, group_size: int) -> str:

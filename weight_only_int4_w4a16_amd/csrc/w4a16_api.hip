@@ -405,6 +405,12 @@ const char* w4a16_status_string(w4a16_status s) {
   return "unknown status";
 }
 
+w4a16_status w4a16_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return W4A16_OK;
+  if (!buf || !sink || bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4)) return W4A16_ERR_ARG;
+  return from_hip(w4a16::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 const char* w4a16_version(void) { return "w4a16-gfx950 0.1"; }
 
 }  // extern "C"

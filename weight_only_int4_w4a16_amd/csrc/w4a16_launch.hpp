@@ -70,6 +70,10 @@ const char* w4a8_name(int M, int K, int N);
 // x'[rows][K] = RN(x * s_inv[k]) (act dtype) into out, 16-byte aligned, K % 8 == 0
 hipError_t launch_awq_scale(const void* x, const void* s_inv, int rows, int K, int act, void* out,
                             hipStream_t stream);
+// streaming read of bytes (a multiple of 16) from buf, folded into sink[kProbeSinkWords]
+// (measurement)
+constexpr int kProbeSinkWords = 256;
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 const char* decode_name(int M, int K, int N, int group_size, int act);
 const char* tiled_name(int M, int K, int N);
 bool tiled_supported(const GemmArgs& a);
