@@ -68,11 +68,15 @@ KERNEL_SOURCES = {
     # kernel family -> the sources that define its code and launch geometry
     "decode": lambda f: f.startswith("w4a16_decode"),
     "tiled": lambda f: f == "w4a16_tiled.hip",
+    "skinny": lambda f: f == "w4a16_skinny.hip",
 }
 
 
 def kernel_family(kernel: str) -> str:
-    return "decode" if kernel.startswith("w4a16_decode") else "tiled"
+    for family in ("decode", "skinny"):
+        if kernel.startswith("w4a16_" + family):
+            return family
+    return "tiled"
 
 
 def source_hash(family: str = "decode") -> str:
