@@ -150,17 +150,23 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     # x beyond the decode kernel's LDS: skinny up to 8192 deep, batched beyond
     assert kernel_name(12, 8192, 57344, 128).startswith("w4a16_skinny")
     assert kernel_name(16, 28672, 8192, 128).startswith("w4a16_tiled")
-    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_decode")     # K N <= 2^24
-    assert kernel_name(32, 4096, 4096, 128).startswith("w4a16_decode")
-    assert kernel_name(33, 4096, 4096, 128).startswith("w4a16_tiled")
-    # 17..32 rows: skinny where its 64-column tiles fill the chip (80 K/4096 <= N/64 <= 512)
+    assert kernel_name(17, 2048, 4096, 128).startswith("w4a16_decode")     # K N < 2^24
+    # 17..128 rows: skinny up to 8192-deep K; at 17..32 rows for up to 512 column tiles, at
+    # 33..128 rows within one launch round and (8192-deep) from 160 column tiles
+    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_skinny")
+    assert kernel_name(32, 4096, 4096, 128).startswith("w4a16_skinny")
+    assert kernel_name(128, 4096, 4096, 128).startswith("w4a16_skinny")
     assert kernel_name(17, 4096, 6144, 128).startswith("w4a16_skinny")
     assert kernel_name(32, 4096, 28672, 128).startswith("w4a16_skinny")
     assert kernel_name(24, 8192, 10240, 128).startswith("w4a16_skinny")
-    assert kernel_name(32, 8192, 8192, 128).startswith("w4a16_tiled")      # 128 tiles < 160
+    assert kernel_name(64, 8192, 10240, 128).startswith("w4a16_skinny")
+    assert kernel_name(32, 8192, 8192, 128).startswith("w4a16_skinny")
+    assert kernel_name(64, 8192, 8192, 128).startswith("w4a16_tiled")      # 128 tiles < 160
     assert kernel_name(32, 8192, 57344, 128).startswith("w4a16_tiled")     # 896 tiles > 512
     assert kernel_name(17, 14336, 4096, 128).startswith("w4a16_tiled")     # deeper than 8192
-    assert kernel_name(33, 4096, 14336, 128).startswith("w4a16_tiled")
+    assert kernel_name(64, 4096, 14336, 128).startswith("w4a16_skinny")
+    assert kernel_name(96, 4096, 14336, 128).startswith("w4a16_tiled")     # 448 workgroups
+    assert kernel_name(129, 4096, 4096, 128).startswith("w4a16_tiled")
 
 
 def test_nf4_requires_codebook(L):
@@ -191,11 +197,10 @@ def test_kernel_name_and_strings(L):
                        (16, 4096, 28672, 128)):
         assert kernel_name(M, K, N, g).endswith("_persist"), (M, K, N, g)
     assert not kernel_name(1, 4096, 28672, 128).endswith("_persist")
-    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_decode")     # K N <= 2^24
-    assert kernel_name(32, 4096, 4096, 128).startswith("w4a16_decode")
-    assert kernel_name(33, 4096, 4096, 128).startswith("w4a16_tiled")
+    assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_skinny")
     assert kernel_name(17, 4096, 6144, 128).startswith("w4a16_skinny")
-    assert kernel_name(65, 4096, 4096, 128).startswith("w4a16_tiled")
+    assert kernel_name(65, 4096, 4096, 128).startswith("w4a16_skinny")
+    assert kernel_name(65, 14336, 4096, 128).startswith("w4a16_tiled")
     # the ragged full-size parity shapes land on each batched geometry (256 compute units)
     assert kernel_name(257, 2080, 44048, 32) == "w4a16_tiled_64x256"
     assert kernel_name(513, 2080, 44048, 32) == "w4a16_tiled_128x512"
@@ -262,7 +267,8 @@ def test_binding_well_shaped_call_reaches_the_device_check():
 def test_binding_gemm_rejects_wrong_shapes(what):
     import torch
     import weight_only_int4_w4a16_amd as w4
-    a = _cpu_affine(M=40, K=4096, N=4096)
+    # (the short-workspace case needs a shape whose kernel takes a workspace: K split)
+    a = _cpu_affine(M=200, K=2048, N=64) if what == "workspace_short" else _cpu_affine(M=40, K=4096, N=4096)
     kw = {}
     if what == "out_rows":
         kw["out"] = torch.zeros((39, 4096), dtype=torch.float16)
@@ -281,7 +287,7 @@ def test_binding_gemm_rejects_wrong_shapes(what):
     elif what == "x_1d":
         a["x"] = torch.zeros(4096, dtype=torch.float16)
     elif what == "workspace_short":
-        need = w4.workspace_bytes(40, 4096, 4096, 128)
+        need = w4.workspace_bytes(200, 2048, 64, 128)
         assert need > 0
         kw["workspace"] = torch.zeros(need - 1, dtype=torch.uint8)
     _raises_arg(lambda: w4.gemm(a["x"], a["packed"], a["scales"], a["qzeros"], a["g"], **kw),

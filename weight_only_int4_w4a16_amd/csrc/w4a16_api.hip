@@ -59,16 +59,37 @@ Path forced_path() {
 // workgroup re-reads x from L2 with each group) leaves the decode kernel: for the skinny kernel
 // when at most 8192 deep (8192x57344 at M=12: 103.6 decode, 90.3 batched, 83.2 us skinny), for
 // the batched kernel otherwise (28672x8192 at M=12: 50.1 decode, 44.8 us batched).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+  }
+  return v;
+}
+
+// Measured on MI355X (fp16 g128, 17..128 rows): the skinny kernel wins wherever its workgroups
+// (64 columns by 32 or 64 rows, all of K) stream at most 8192-deep K and fit in one launch
+// round, by 10-40% (4096x14336 at M=64: 19.1 against 25.5 us; 4096x4096 at M=128: 15.7
+// against 23.0 us); at 17-32 rows also in two rounds (8192x28672 at M=32: 44.7 against 49.4
+// us). At 33+ rows on 8192-deep K with fewer than 160 column tiles the batched kernel's split
+// K wins (8192x8192 at M=64: 21.9 against 26.4 us), and so it does for deeper K and wider N.
 Path choose_path(const GemmArgs& a) {
   const Path f = forced_path();
   if (f != PATH_AUTO) return f;
   const long long kn = (long long)a.K * a.N;
-  const int col_tiles = a.N / 64;
-  const bool skinny_fits = a.K <= 8192 && (long long)col_tiles * 4096 >= 80LL * a.K && col_tiles <= 512;
-  if (a.M > 32) return PATH_TILED;
+  const long long col_tiles = (a.N + 63) / 64;
+  if (a.M > 128) return PATH_TILED;
   if (a.M > 16) {
-    if (kn <= (1LL << 24)) return PATH_DECODE;
-    return skinny_fits ? PATH_SKINNY : PATH_TILED;
+    if (a.M <= 32 && kn < (1LL << 24)) return PATH_DECODE;
+    if (a.K > 8192) return PATH_TILED;
+    if (a.M <= 32) return col_tiles <= 512 ? PATH_SKINNY : PATH_TILED;
+    const long long wgs = col_tiles * ((a.M + 63) / 64);
+    return wgs <= device_cus() && (a.K <= 4096 || col_tiles >= 160) ? PATH_SKINNY : PATH_TILED;
   }
   if (a.M < 12 || kn < (1LL << 27)) return PATH_DECODE;
   if (w4a16::decode_config(a.M, a.K, a.N, a.group_size, a.glu).x_in_lds) return PATH_DECODE;

@@ -1,27 +1,31 @@
 // w4a16_skinny.hip - W4A16 GEMM for mid-size batches (17 to 64 rows): the weight bytes still
-// bound the time, but each weight now feeds enough rows that the MFMAs and the activation
-// reads matter too.
+// bound the time, but each weight now feeds enough rows that the activation reads and the
+// MFMAs matter too.
 //
 // "INT8 vs INT4 Quantization, in depth", section "Two regimes": below the crossover batch a
 // layer waits on its weight bytes, so the codes must stream at full rate while every row of x
 // is multiplied on-chip; "4.3 Weight-only INT4", section 4 (Marlin): the speedup holds near
 // its ceiling at batch 16-32 only if the kernel keeps enough loads in flight.
 //
-// Work split. A workgroup owns NP pairs of 16-column strips (32 NP columns) and up to 32 MT
-// rows over the whole K range; its W waves take W contiguous k-block slices of K, each wave
-// streaming the codes of all NP pairs and the activation fragments of all MT row tiles for its
-// slice. No wave waits for another until the end, where the W partial tiles are summed through
-// LDS in wave order (deterministic, no global partials, no second launch). A column tile is
-// thus read by one workgroup with W independent load streams, which keeps about W x 20 KB in
-// flight per compute unit.
+// Work split. A workgroup owns two pairs of 16-column strips (64 columns) and up to 32 MT rows
+// over the whole K range; its eight waves take eight contiguous k-block slices of K. No wave
+// waits for another until the end, where the eight partial tiles are summed through LDS in
+// wave order (deterministic, no global partials, no second launch).
+//
+// Two load streams per wave, each sized for where it comes from.
+// - Codes (HBM): whole 16-byte chunks, two per lane per pair and block, into four register
+//   sets, so three blocks (12 KiB per wave) are in flight while one is multiplied.
+// - Activations (L2: every workgroup reads all of x): half blocks (32 MT rows x 64 k) copied
+//   from global memory straight into a per-wave LDS ring (global_load_lds_dwordx4, eight rows
+//   of 128 bytes per instruction, so every request is a whole cache line). Row r of a slot
+//   holds its eight 16-byte chunks at positions c ^ (r/2 % 8), so the fragment reads of
+//   sixteen consecutive rows fall in sixteen different bank groups. Only the wave that fills
+//   a slot reads it, so its own load counter orders the two and no barrier is needed.
 //
 // Operands. v_mfma_f32_32x32x16_{f16,bf16}: lane l multiplies row l%32 of a row tile with
 // column l%32 of a strip pair, k = 16t + 8(l/32) .. +8 at step t of a 128-k block. The codes of
-// those k are word t/2 of the packed chunk lane 16((2t + l/32) % 4) + l%16 owns (two 16-byte
-// chunks per lane per pair and block, as in the batched kernel). The activation fragment is
-// 16 contiguous bytes of one row of x, loaded straight from global memory (L2): a wave's
-// slice of x is its own, so staging it in LDS would save nothing. Each word is dequantized
-// once per workgroup and used for MT row tiles.
+// those k are word t/2 of the packed chunk lane 16((2t + l/32) % 4) + l%16 owns (as in the
+// batched kernel). Each word is dequantized once per workgroup and used for MT row tiles.
 #include "w4a16_device.hpp"
 #include "w4a16_launch.hpp"
 
@@ -52,15 +56,48 @@ struct SkinnyParams {
   int half;         // GLU: strips per half of the fused gate+up weight (NT / 2)
 };
 
-// GLU: NP = 2, pair 0 holds two gate strips and pair 1 the matching up strips; the output is
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyPairs = 2;
+constexpr int kCodeSets = 4;  // code register sets: the block multiplied and three in flight
+// activation slots (half blocks) per wave: 4 for one row tile, 2 for two (16 KiB either way)
+constexpr int skinny_slots(int MT) { return MT == 1 ? 4 : 2; }
+constexpr int skinny_slot_halves(int MT) { return 32 * MT * 64; }
+constexpr int skinny_ring_halves(int MT) { return skinny_slots(MT) * skinny_slot_halves(MT); }
+constexpr size_t skinny_lds_bytes(int MT) { return (size_t)kSkinnyWaves * skinny_ring_halves(MT) * 2; }
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int n>
+__device__ __forceinline__ void skinny_wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt holds 0..63");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Sixteen zero bytes in device memory: the source of the activation chunks past a ragged K.
+__device__ __attribute__((aligned(16))) const uint16_t kSkinnyZero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes dst + 16 l (dst is
+// the same for the whole wave)
+__device__ __forceinline__ void skinny_copy16(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// GLU: pair 0 holds two gate strips and pair 1 the matching up strips; the output is
 // h = SiLU(gate) * up, [M][N/2].
-template <int ACT, int GPC, int FMT, int MT, int NP, int W, bool GLU>
-__global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
+template <int ACT, int GPC, int FMT, int MT, bool GLU>
+__global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_kernel(SkinnyParams p) {
   typedef typename ActT<ACT>::type AT;
-  static_assert(!GLU || NP == 2, "a SwiGLU tile is one gate pair and one up pair");
+  constexpr int W = kSkinnyWaves, NP = kSkinnyPairs, RB = kCodeSets, RA = skinny_slots(MT);
   constexpr bool ZEROS = FMT == FMT_ASYM;
-  constexpr int TILE = MT * NP * 1024;  // fp32 partial sums per wave
-  extern __shared__ __attribute__((aligned(16))) float red[];  // [W][MT][NP][16][64]
+  constexpr int SLOT = skinny_slot_halves(MT);
+  constexpr int RING = skinny_ring_halves(MT);
+  constexpr int KX = 4 * MT;                            // copy instructions per slot
+  constexpr int KB = NP * 2 + NP * GPC * (ZEROS ? 2 : 1);  // load instructions per code block
+  constexpr int TILE = MT * NP * 1024;                  // fp32 partial sums per wave
+  static_assert(TILE * 4 <= RING * 2, "a wave's partial tile fits in its ring");
+  static_assert(RA % 2 == 0 && (2 * RB) % RA == 0, "the unrolled step count covers both rings");
+  constexpr int U = 2 * RB;                             // half blocks per unrolled pass
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [W][RA][32 MT][64]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -70,6 +107,8 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
   const int kc0 = min(wave * p.slice, KC);
   const int kc1 = min(kc0 + p.slice, KC);
   const int nb = kc1 - kc0;
+  const int nh = 2 * nb;  // half blocks of this wave
+  uint16_t* const ring = lds + (size_t)wave * RING;
   const int h16 = (lane >> 4) & 1;  // which strip of a pair this lane's column is in
   // strip of pair pr for this lane, clamped in bounds for loads (never stored past N)
   auto strip_of = [&](int pr) __attribute__((always_inline)) {
@@ -77,49 +116,59 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
   };
   const int shift = 4 * (lane & 7);
   const int c0 = 16 * (lane >> 5) + (lane & 15);  // first packed chunk of this lane
-
-  // A pipeline stage is half a k-block (64 k, four MFMA steps): the A fragments of its steps,
-  // words 2 hf and 2 hf + 1 of the lane's two packed chunks (8 bytes each), and the scale
-  // groups it spans
-  constexpr int GPH = GPC >= 2 ? GPC / 2 : 1;  // scale groups per half block
-  typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
-  struct Regs {
-    u4_t a[MT][4];          // activation fragments, row tile mt, step t of the half
-    u2_t b[NP][2];          // words (2 hf, 2 hf + 1) of chunks c0 and c0 + 32
-    uint32_t s[NP][GPH];    // 16-bit scale (NF4: absmax), zero-extended by the load
-    uint32_t z[NP][GPH];
-  };
   int col[NP];
 #pragma unroll
   for (int pr = 0; pr < NP; ++pr) col[pr] = strip_of(pr) * 16 + (lane & 15);
-  int xrow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xrow[mt] = min(m0 + mt * 32 + (lane & 31), M - 1);
 
-  // stage s of this wave: k-block kc0 + s / 2, half s % 2
-  auto load = [&](Regs& R, int st) __attribute__((always_inline)) {
-    const int kc = kc0 + (st >> 1), hf = st & 1;
+  // activation copies: instruction j of a slot covers its rows 8j .. 8j+7, lane l row
+  // 8j + l/8 and position l%8, which holds 16-byte chunk (l%8) ^ (row/2 % 8) of the row's half
+  // block (rows past M repeat row M-1 and are never stored)
+  const uint16_t* xsrc[KX];  // this lane's chunk of the slice's first half, per instruction
+  int xoff[KX];
+#pragma unroll
+  for (int j = 0; j < KX; ++j) {
+    const int row = 8 * j + (lane >> 3);
+    xoff[j] = kc0 * 128 + ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+    xsrc[j] = p.x + (size_t)min(m0 + row, M - 1) * K + xoff[j];
+  }
+  auto load_x = [&](int h, int slot) __attribute__((always_inline)) {
+    const int kh = 64 * h;  // wave-uniform
+    if (kc0 * 128 + kh + 64 <= K) {  // the whole half lies below K
+#pragma unroll
+      for (int j = 0; j < KX; ++j) skinny_copy16(xsrc[j] + kh, ring + slot * SLOT + j * 512);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KX; ++j)
+        skinny_copy16(xoff[j] + kh < K ? xsrc[j] + kh : kSkinnyZero, ring + slot * SLOT + j * 512);
+    }
+  };
+
+  struct Codes {
+    u4_t b[NP][2];          // chunks c0 and c0 + 32 of the lane's strip
+    uint16_t s[NP][GPC];    // scale (NF4: absmax)
+    uint32_t z[NP][GPC];
+  };
+  // per-lane bases; each load adds a wave-uniform offset
+  const u4_t* bsrc[NP];
+  const uint16_t* ssrc[NP];
+  const uint32_t* zsrc[NP];
+#pragma unroll
+  for (int pr = 0; pr < NP; ++pr) {
+    bsrc[pr] = p.packed + (size_t)(col[pr] >> 4) * KC * 64 + c0;
+    ssrc[pr] = p.scales + col[pr];
+    zsrc[pr] = p.qzeros + (col[pr] >> 3);
+  }
+  auto load_b = [&](Codes& R, int kc) __attribute__((always_inline)) {
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
-      const u2_t* blk = reinterpret_cast<const u2_t*>(p.packed + ((size_t)(col[pr] >> 4) * KC + kc) * 64);
-      R.b[pr][0] = blk[2 * c0 + hf];
-      R.b[pr][1] = blk[2 * (c0 + 32) + hf];
+      const u4_t* blk = bsrc[pr] + (size_t)kc * 64;
+      R.b[pr][0] = __builtin_nontemporal_load(blk);
+      R.b[pr][1] = __builtin_nontemporal_load(blk + 32);
 #pragma unroll
-      for (int gl = 0; gl < GPH; ++gl) {
-        const int gi = GPC >= 2 ? hf * GPH + gl : 0;
+      for (int gi = 0; gi < GPC; ++gi) {
         const int g = min(kc * GPC + gi, p.NG - 1);  // groups past K are never used
-        R.s[pr][gl] = p.scales[(size_t)g * N + col[pr]];
-        if constexpr (ZEROS) R.z[pr][gl] = p.qzeros[(size_t)g * (N >> 3) + (col[pr] >> 3)];
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* xr = p.x + (size_t)xrow[mt] * K + (lane >> 5) * 8;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        // a ragged K ends inside the last block: read an in-bounds chunk, zeroed in compute
-        const int k = min(kc * 128 + 64 * hf + 16 * t, K - 16);
-        R.a[mt][t] = *reinterpret_cast<const u4_t*>(xr + k);
+        R.s[pr][gi] = ssrc[pr][(size_t)g * N];
+        if constexpr (ZEROS) R.z[pr][gi] = zsrc[pr][(size_t)g * (N >> 3)];
       }
     }
   };
@@ -135,82 +184,104 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][pr][i] = 0.f;
 
-  auto compute = [&](const Regs& R, int st) __attribute__((always_inline)) {
-    const int kc = kc0 + (st >> 1), hf = st & 1;
-    const int kvalid = K - kc * 128 - 64 * hf;  // k of this half below K (a multiple of 32)
+  // half hf of a block: its four 16-k steps, codes from R, activations from one slot (the
+  // chunks past a ragged K are zeros, so their products vanish)
+  auto compute_half = [&](const Codes& R, int hf, int slot) __attribute__((always_inline)) {
+    const uint16_t* xs = ring + slot * SLOT;
+    // the half's activation fragments first (one LDS wait for all four steps): step t, row
+    // tile mt is row 32 mt + l%32, chunk 2t + l/32
+    u4_t af[4][MT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 32 + (lane & 31);
+        const int c = 2 * t + (lane >> 5);
+        af[t][mt] = *reinterpret_cast<const u4_t*>(xs + row * 64 + ((c ^ ((row >> 1) & 7)) * 8));
+      }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      // step 4 hf + t: word (4 hf + t) / 2 of chunk c0 (even steps) or c0 + 32 (odd)
-      const int gl = GPC >= 2 ? t / (8 / GPC) : 0;
+      const int st = 4 * hf + t;  // step of the block: word st/2 of chunk st%2
+      const int gi = GPC >= 2 ? st / (8 / GPC) : 0;
       AT bf[NP];
 #pragma unroll
       for (int pr = 0; pr < NP; ++pr) {
-        const uint32_t w = R.b[pr][t & 1][t >> 1];
-        const uint32_t sraw = R.s[pr][gl];
+        const uint32_t w = R.b[pr][st & 1][st >> 1];
+        const uint32_t sraw = R.s[pr][gi];
         if constexpr (FMT == FMT_NF4) {
           if constexpr (ACT == ACT_F16)
             bf[pr] = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
           else
             bf[pr] = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
         } else {
-          const uint32_t zq = ZEROS ? (R.z[pr][gl] >> shift) & 0xFu : 8u;
+          const uint32_t zq = ZEROS ? (R.z[pr][gi] >> shift) & 0xFu : 8u;
           if constexpr (ACT == ACT_F16)
             bf[pr] = dequant_word_f16(w, make_zero_f16(zq), as_h2(sraw * 0x00010001u));
           else
             bf[pr] = dequant_word_bf16(w, make_zero_f32(zq, __builtin_bit_cast(float, sraw << 16)));
         }
       }
-      const bool in_k = 16 * t < kvalid;  // the step's 16 k are all in, or all out
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const u4_t a = in_k ? R.a[mt][t] : u4_t{0u, 0u, 0u, 0u};
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int pr = 0; pr < NP; ++pr)
-          acc[mt][pr] = mfma32(__builtin_bit_cast(AT, a), bf[pr], acc[mt][pr]);
-      }
+          acc[mt][pr] = mfma32(__builtin_bit_cast(AT, af[t][mt]), bf[pr], acc[mt][pr]);
     }
   };
 
-  // ST register sets of half blocks: stages s+1 .. s+ST-1 load while stage s is multiplied
-  // (measured: four sets at 32 rows cost 5-20% against two, from the lower occupancy). Loads
-  // are unconditional (past the slice they re-read its last half, never
-  // used), so the in-order load counter only ever waits for the set about to be used; a
-  // scheduling barrier after each batch of loads keeps the compiler from sinking them below the
-  // MFMAs.
-  constexpr int ST = 2;
-  const int ns = 2 * nb;  // stages of this wave (even)
-  if (ns > 0) {
-    Regs R[ST];
-#pragma unroll
-    for (int u = 0; u + 1 < ST; ++u) load(R[u], min(u, ns - 1));
-    int st = 0;
-    for (; st + ST - 1 < ns; st += ST) {
-#pragma unroll
-      for (int u = 0; u < ST; ++u) {
-        load(R[(u + ST - 1) % ST], min(st + u + ST - 1, ns - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(R[u], st + u);
-      }
+  // Step h (half block h of the slice) issues the copies of half h + RA - 1 and, on even h,
+  // the codes of block h/2 + RB - 1, then multiplies half h (slot h % RA, code set h/2 % RB).
+  // Loads past the slice re-read its last half or block (never used), and the steps run in
+  // whole passes of U (those past the slice multiply nothing), so every step issues the same
+  // instructions with no branch around them and the in-order load counter counts exactly:
+  // after half h's copies come RA - 1 steps' copies and RA/2 code blocks. The prologue
+  // interleaves its copies and code blocks so that the count holds from the first step.
+  if (nh > 0) {
+    Codes R[RB];
+    static_assert(RB == 4 && (RA == 4 || RA == 2), "the prologue order below");
+    auto pro_b = [&](int j) __attribute__((always_inline)) {
+      load_b(R[j], kc0 + min(j, nb - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pro_x = [&](int q) __attribute__((always_inline)) {
+      load_x(min(q, nh - 1), q);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (RA == 4) {
+      pro_b(0); pro_b(1); pro_x(0); pro_x(1); pro_b(2); pro_x(2);
+    } else {
+      pro_b(0); pro_b(1); pro_b(2); pro_x(0);
     }
+    const int passes = (nh + U - 1) / U;
+    for (int ps = 0; ps < passes; ++ps) {
+      const int h0 = ps * U;
 #pragma unroll
-    for (int u = 0; u + 1 < ST; ++u) {
-      if (st + u < ns) {
-        load(R[(u + ST - 1) % ST], min(st + u + ST - 1, ns - 1));
+      for (int u = 0; u < U; ++u) {
+        const int h = h0 + u;
+        load_x(min(h + RA - 1, nh - 1), (u + RA - 1) % RA);
+        __builtin_amdgcn_sched_barrier(0);  // the count below assumes copies, then codes
+        if (u % 2 == 0) load_b(R[(u / 2 + RB - 1) % RB], kc0 + min(h / 2 + RB - 1, nb - 1));
         __builtin_amdgcn_sched_barrier(0);
-        compute(R[u], st + u);
+        skinny_wait_vmcnt<(RA - 1) * KX + (RA / 2) * KB>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (h < nh) compute_half(R[(u / 2) % RB], u % 2, u % RA);
       }
     }
   }
 
   // ---- the W partial tiles, summed through LDS in wave order ----
+  // Each wave writes its tile over its own ring, once its copies there have landed.
   // lane l holds column l%32 of pair pr and rows 32 mt + 8 (i/4) + 4 (l/32) + i%4, i < 16
+  constexpr int RED = RING / 2;  // floats per wave region
+  float* red = reinterpret_cast<float*>(lds);
+  skinny_wait_vmcnt<0>();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        red[(size_t)wave * TILE + ((mt * NP + pr) * 16 + i) * 64 + lane] = acc[mt][pr][i];
+        red[(size_t)wave * RED + ((mt * NP + pr) * 16 + i) * 64 + lane] = acc[mt][pr][i];
   __syncthreads();
   constexpr int OUT_TILES = GLU ? MT : MT * NP;  // GLU: gate tiles (pr = 0) only
   for (int e = threadIdx.x; e < OUT_TILES * 1024; e += 64 * W) {
@@ -221,8 +292,8 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
     const int e0 = ((mt * NP + pr) * 16 + i) * 64 + l;
     float v = 0.f, u = 0.f;
     for (int w = 0; w < W; ++w) {
-      v += red[(size_t)w * TILE + e0];
-      if constexpr (GLU) u += red[(size_t)w * TILE + e0 + 16 * 64];
+      v += red[(size_t)w * RED + e0];
+      if constexpr (GLU) u += red[(size_t)w * RED + e0 + 16 * 64];
     }
     if (m >= M) continue;
     if constexpr (GLU) {
@@ -238,7 +309,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(SkinnyParams p) {
 }
 
 struct SkinnyGeometry {
-  int MT, NP, W;
+  int MT;
   int tiles_n, tiles_m, slice;
   size_t lds_bytes;
 };
@@ -246,21 +317,18 @@ struct SkinnyGeometry {
 SkinnyGeometry skinny_geometry(int M, int K, int N, bool glu) {
   SkinnyGeometry g;
   g.MT = M <= 32 ? 1 : 2;
-  g.NP = 2;
-  g.W = 8;
   const int KC = ceil_div(K, 128);
-  g.tiles_n = glu ? (N / 2) / 32 + ((N / 2) % 32 ? 1 : 0) : ceil_div(N, 32 * g.NP);
+  g.tiles_n = glu ? (N / 2) / 32 + ((N / 2) % 32 ? 1 : 0) : ceil_div(N, 32 * kSkinnyPairs);
   g.tiles_m = ceil_div(M, 32 * g.MT);
-  g.slice = ceil_div(KC, g.W);
-  g.lds_bytes = (size_t)g.W * g.MT * g.NP * 1024 * 4;
+  g.slice = ceil_div(KC, kSkinnyWaves);
+  g.lds_bytes = skinny_lds_bytes(g.MT);
   return g;
 }
 
 template <int ACT, int GPC, int FMT, int MT, bool GLU>
 hipError_t launch_cfg(const SkinnyParams& p, const SkinnyGeometry& g, hipStream_t s) {
-  constexpr int NP = 2, W = 8;
-  hipLaunchKernelGGL((skinny_kernel<ACT, GPC, FMT, MT, NP, W, GLU>), dim3(g.tiles_n, g.tiles_m),
-                     dim3(64 * W), g.lds_bytes, s, p);
+  hipLaunchKernelGGL((skinny_kernel<ACT, GPC, FMT, MT, GLU>), dim3(g.tiles_n, g.tiles_m),
+                     dim3(64 * kSkinnyWaves), g.lds_bytes, s, p);
   return hipGetLastError();
 }
 

@@ -19,6 +19,12 @@
 // and shared by the four waves; the A fragment of a row tile is read once per step and
 // used for both pairs. Accumulation is fp32.
 //
+// k-groups. A small-tile workgroup that has its compute unit to itself runs two sets of four
+// waves (two waves per SIMD) that take the two halves of its K range, each with its own ring
+// of activation tiles. The second set's fp32 tiles pass through LDS to the first, which adds
+// them (in a fixed order) and stores. A second wave per SIMD issues its dequantization while
+// the other's MFMAs run (4096x14336 at M=256: 46.2 -> 42.8 us; M=192: 50.5 -> 40.0 us).
+//
 // Split-K. When the output tiles alone cannot fill the chip, the K range is cut into S
 // contiguous slices, one workgroup each. Every slice stores its fp32 partial tile in the
 // workspace and a second small kernel sums the S partials in slice order (deterministic)
@@ -38,18 +44,22 @@ namespace {
 // strip pairs. Large: 128 x 512, eight waves (two per SIMD) of two pairs. Small: 64 x 256, four
 // waves of two pairs, for GEMMs whose large tiles would leave compute units idle (each large
 // tile row of M <= 256 is 28-56 tiles at N = 14336).
-template <int MT, int WAVES, int NP, int STAGES>
+template <int MT, int WAVES, int NP, int STAGES, int KG = 1>
 struct TileShape {
   static constexpr int kStages = STAGES;  // blocks in flight: LDS slots and code register sets
   static constexpr int kMT = MT;
   static constexpr int kBM = 32 * MT;
   static constexpr int kNP = NP;
   static constexpr int kBN = 32 * NP * WAVES;
-  static constexpr int kWaves = WAVES;
-  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int kWaves = WAVES;    // waves of one k-group (each owns 64 NP/2 columns)
+  static constexpr int kKG = KG;          // k-groups: wave sets that split the tile's K range
+  static constexpr int kThreads = 64 * WAVES * KG;
   static constexpr int kADma = kBM / 4 / WAVES;  // 1 KiB direct-to-LDS loads per wave per block
   static constexpr size_t kSlotBytes = (size_t)kBM * 256;       // one activation tile
-  static constexpr size_t kLdsBytes = kStages * kSlotBytes;     // the ring of tiles
+  static constexpr size_t kRingBytes = kStages * kSlotBytes;    // a k-group's ring of tiles
+  // the rings, which the later k-groups' fp32 tiles reuse at the end
+  static constexpr size_t kRedBytes = (size_t)(KG - 1) * WAVES * MT * NP * 16 * 64 * 4;
+  static constexpr size_t kLdsBytes = KG * kRingBytes > kRedBytes ? KG * kRingBytes : kRedBytes;
   static_assert(kADma * WAVES * 4 == kBM, "the tile's rows split evenly over the waves");
 };
 // Stages: a small tile's block takes about one HBM round trip to multiply, so a workgroup that
@@ -57,10 +67,13 @@ struct TileShape {
 // workgroup: 47.2 -> 43.7, 48.2 -> 45.4 us against one block ahead); with K split into short
 // slices (8 blocks) the deeper prologue costs more than it hides (5-10%), so those keep one
 // block ahead. The large tile's 128 accumulators leave registers for one block ahead, which
-// its four-times-longer blocks cover.
+// its four-times-longer blocks cover. Two k-groups keep one block ahead each: their waves may
+// hold at most 256 registers, which three register sets exceed for most formats, and the
+// second wave per SIMD covers the latency (three blocks ahead measured no faster).
 typedef TileShape<4, 8, 2, 2> LargeTile;
 typedef TileShape<2, 4, 2, 2> SmallTile;
 typedef TileShape<2, 4, 2, 4> SmallTileDeep;
+typedef TileShape<2, 4, 2, 2, 2> SmallTile2;
 constexpr int kDeepBlocks = 16;  // k-blocks per workgroup from which the small tile goes deep
 
 enum Fmt { FMT_ASYM = 0, FMT_SYM = 1, FMT_NF4 = 2 };
@@ -130,7 +143,8 @@ __device__ __forceinline__ void copy16_to_lds(const uint16_t* src, uint16_t* dst
 template <int ACT, int GPC, int FMT, class T, bool GLU>
 __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   constexpr int kMT = T::kMT, kBM = T::kBM, kWaves = T::kWaves, kADma = T::kADma;
-  constexpr int kPairs = T::kNP, kStrips = 2 * T::kNP, kStages = T::kStages;
+  constexpr int kPairs = T::kNP, kStrips = 2 * T::kNP, kStages = T::kStages, kKG = T::kKG;
+  static_assert(kKG == 1 || kKG == 2, "k-groups differ by at most one block");
   static_assert(!GLU || kPairs == 2, "a SwiGLU wave holds a gate pair and an up pair");
   typedef typename ActT<ACT>::type AT;
   constexpr bool ZEROS = FMT == FMT_ASYM;
@@ -138,18 +152,27 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   // code chunks per pair, and per pair and scale group a scale (and a zero word); and in all
   constexpr int kLoadsAfterCopies = kPairs * 2 + kPairs * GPC * (ZEROS ? 2 : 1);
   constexpr int kLoadsPerBlock = kADma + kLoadsAfterCopies;
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds_a[];  // [kStages][kBM][128]
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [kKG][kStages][kBM][128]
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kg = wave_id / kWaves;              // this wave's k-group
+  const int wave = wave_id - kg * kWaves;       // and its column role within the group
+  uint16_t* const lds_a = lds + (size_t)kg * kStages * kBM * 128;  // the group's ring
   const int tiles = p.tiles_m * p.tiles_n;
   const int t = tile_of(blockIdx.x, tiles);
   const int tm = t % p.tiles_m, tn = t / p.tiles_m;  // neighbours share weight columns
   const int z = blockIdx.y;
   const int K = p.K, N = p.N, M = p.M, KC = p.KC;
   const int m0 = tm * kBM;
+  // the workgroup's K slice [kc0, kc1), and this k-group's part of it [kb0, kb0 + nbg): the
+  // groups take ceil(n / kKG) contiguous blocks each, the last possibly one fewer (or none)
   const int kc0 = z * p.kps;
   const int kc1 = min(kc0 + p.kps, KC);
+  const int nbh = (kc1 - kc0 + kKG - 1) / kKG;
+  const int kb0 = kc0 + kg * nbh;
+  const int nbg = max(min(kb0 + nbh, kc1) - kb0, 0);
+  const int klast = nbg > 0 ? kb0 + nbg - 1 : kc1 - 1;  // loads past the part re-read this block
   const int nt0 = tn * (kWaves * kStrips) + wave * kStrips;  // this wave's first strip
   const int g0 = tn * (kWaves * 2) + wave * 2;                // GLU: its first gate strip
   // strip of pair pr, half h (h = lane/16 % 2), clamped in bounds for loads
@@ -291,30 +314,64 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   // block, never used), so every wave issues the same vector-memory instructions per block
   // and the wait count is exact: after block i's copies come its own code loads and the
   // kStages-2 later blocks' loads.
-  const int nb = kc1 - kc0;
-  const int kl = kc1 - 1;
+  // Every wave of the workgroup runs nbh block steps (one barrier each); a k-group with one
+  // block fewer loads its last block again in its final step and skips the multiply.
+  const int nb_min = max(kc1 - kc0 - (kKG - 1) * nbh, 0);  // blocks of the last group
   Regs R[kStages];
 #pragma unroll
-  for (int st = 0; st + 1 < kStages; ++st) load(R[st], min(kc0 + st, kl), st);
-  auto step_block = [&](const Regs& Rb, Regs& Rfree, int i, int slot) __attribute__((always_inline)) {
+  for (int st = 0; st + 1 < kStages; ++st) load(R[st], min(kb0 + st, klast), st);
+  auto step_block = [&](const Regs& Rb, Regs& Rfree, int i, int slot, bool live) __attribute__((always_inline)) {
     wait_vmcnt<kLoadsAfterCopies + (kStages - 2) * kLoadsPerBlock>();  // block i's copies landed
     __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no LDS access moves across the barrier
     __builtin_amdgcn_s_barrier();             // every wave's copies of block i are in LDS, and
                                               // every wave is done with block i-1's slot
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
-    load(Rfree, min(kc0 + i + kStages - 1, kl), (slot + kStages - 1) % kStages);
-    compute(Rb, slot);
+    load(Rfree, min(kb0 + i + kStages - 1, klast), (slot + kStages - 1) % kStages);
+    if (live) compute(Rb, slot);
   };
   int i = 0;
-  for (; i + kStages - 1 < nb; i += kStages) {
+  for (; i + kStages <= nb_min; i += kStages) {
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) step_block(R[u], R[(u + kStages - 1) % kStages], i + u, u);
+    for (int u = 0; u < kStages; ++u) step_block(R[u], R[(u + kStages - 1) % kStages], i + u, u, true);
   }
+  // at most kStages steps remain (kStages - 1, and the one more of a longer k-group); the
+  // step count is the workgroup's, so every wave meets the same barriers
 #pragma unroll
-  for (int u = 0; u + 1 < kStages; ++u)
-    if (i + u < nb) step_block(R[u], R[(u + kStages - 1) % kStages], i + u, u);
+  for (int u = 0; u < kStages; ++u)
+    if (i + u < nbh) step_block(R[u], R[(u + kStages - 1) % kStages], i + u, u, i + u < nbg);
   // the loads still in flight (re-reads past the slice) retire before the wave ends
+
+  // k-groups: the later groups' fp32 tiles go through LDS (over the rings, once every
+  // wave's copies have landed and every wave is done with its slots) and group 0 adds them
+  // in group order
+  if constexpr (kKG > 1) {
+    constexpr int kTile = kMT * kPairs * 16 * 64;  // floats per wave
+    float* red = reinterpret_cast<float*>(lds);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kg > 0) {
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int pr = 0; pr < kPairs; ++pr)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            red[(size_t)((kg - 1) * kWaves + wave) * kTile + ((mt * kPairs + pr) * 16 + e) * 64 + lane] =
+                acc[mt][pr][e];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < kKG; ++g)
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int pr = 0; pr < kPairs; ++pr)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            acc[mt][pr][e] += red[(size_t)((g - 1) * kWaves + wave) * kTile + ((mt * kPairs + pr) * 16 + e) * 64 + lane];
+  }
 
   // ---- epilogue ----
   // lane l holds column 32*pair + l%32 and rows 32*mt + 8*(i/4) + 4*(l/32) + i%4, i < 16
@@ -414,12 +471,14 @@ struct TiledGeometry {
   int kind;            // TileKind
   int bm, bn;          // tile rows and columns
   int tiles_m, tiles_n, S, kps;
+  int kg;              // k-groups per workgroup (small tile: 1 or 2)
   size_t partial_bytes;
 };
 
 // A tile kind with K cut into (about) S contiguous slices of whole k-blocks.
-TiledGeometry geometry_for(int M, int K, int N, int kind, int S) {
+TiledGeometry geometry_for(int M, int K, int N, int kind, int S, int kg) {
   TiledGeometry g;
+  g.kg = kg;
   const int KC = ceil_div(K, 128);
   g.kind = kind;
   g.bm = kind == TILE_LARGE ? LargeTile::kBM : SmallTile::kBM;
@@ -437,15 +496,31 @@ TiledGeometry geometry_for(int M, int K, int N, int kind, int S) {
 // rate one compute unit sustains with that tile; when K is split, the fp32 partial sums are
 // written and read back at 5 TB/s and the reduce launch costs 2 us. Rates measured on MI355X
 // (fp16, g128): large tile 4.2-5.4 TFLOP/s per compute unit (4.6 taken); small tile 2.7 with
-// one workgroup per compute unit, 3.4 with two or more.
+// one workgroup per compute unit, 3.4 with two or more, 4.0 with two k-groups (which the
+// search offers only where every workgroup has a compute unit to itself).
 double modelled_us(const TiledGeometry& g, int M, int N, int cus) {
   const long wgs = (long)g.tiles_m * g.tiles_n * g.S;
   const long per_cu = (wgs + cus - 1) / cus;
   const double wg_flops = 2.0 * g.bm * g.bn * g.kps * 128;
-  const double rate = g.kind == TILE_LARGE ? 4.6e6 : per_cu > 1 ? 3.4e6 : 2.7e6;  // flop per us
+  const double rate = g.kind == TILE_LARGE ? 4.6e6
+                      : g.kg == 2            ? 4.0e6
+                      : per_cu > 1           ? 3.4e6
+                                             : 2.7e6;  // flop per us
   double us = per_cu * (2.5 + wg_flops / rate);
   if (g.S > 1) us += 2.0 * g.S * M * (double)N * 4 / 5e6 + 2.0;
   return us;
+}
+
+// W4A16_FORCE_KG=1|2 pins the small tile's k-groups the same way.
+int forced_kg() {
+  static const int forced = [] {
+    const char* v = getenv("W4A16_FORCE_KG");
+    if (!v) return 0;
+    if (!strcmp(v, "1")) return 1;
+    if (!strcmp(v, "2")) return 2;
+    return 0;
+  }();
+  return forced;
 }
 
 // W4A16_FORCE_TILE=large|small pins the batched kernel's tile kind (its K split is still
@@ -470,18 +545,23 @@ int forced_tile() {
 TiledGeometry tiled_geometry(int M, int K, int N) {
   const int cus = cu_count_tiled();
   const int KC = ceil_div(K, 128);
-  const int f = forced_tile();
+  const int f = forced_tile(), fkg = forced_kg();
   TiledGeometry best{};
   double best_us = -1;
   for (int kind = 0; kind < 2; ++kind) {
     if (f >= 0 && kind != f) continue;
-    for (int S = 1; S == 1 || KC / S >= 2; S *= 2) {
-      const TiledGeometry g = geometry_for(M, K, N, kind, S);
-      if (S > 1 && (long)g.tiles_m * g.tiles_n * g.S > 4L * cus) break;
-      const double us = modelled_us(g, M, N, cus);
-      if (best_us < 0 || us < best_us) {
-        best = g;
-        best_us = us;
+    for (int kg = 1; kg <= (kind == TILE_SMALL ? 2 : 1); ++kg) {
+      if (fkg && kind == TILE_SMALL && kg != fkg) continue;
+      for (int S = 1; S == 1 || KC / S >= 2 * kg; S *= 2) {
+        const TiledGeometry g = geometry_for(M, K, N, kind, S, kg);
+        const long wgs = (long)g.tiles_m * g.tiles_n * g.S;
+        if (S > 1 && wgs > 4L * cus) break;
+        if (kg == 2 && wgs > cus) break;  // two k-groups only where one workgroup per CU is left
+        const double us = modelled_us(g, M, N, cus);
+        if (best_us < 0 || us < best_us) {
+          best = g;
+          best_us = us;
+        }
       }
     }
   }
@@ -529,6 +609,8 @@ bool tiled_supported(const GemmArgs&) { return true; }
 
 const char* tiled_name(int M, int K, int N) {
   const TiledGeometry g = tiled_geometry(M, K, N);
+  if (g.kind == TILE_SMALL && g.kg == 2)
+    return g.S > 1 ? "w4a16_tiled_64x256_kg2_splitk" : "w4a16_tiled_64x256_kg2";
   if (g.kind == TILE_SMALL) return g.S > 1 ? "w4a16_tiled_64x256_splitk" : "w4a16_tiled_64x256";
   return g.S > 1 ? "w4a16_tiled_128x512_splitk" : "w4a16_tiled_128x512";
 }
@@ -575,6 +657,7 @@ hipError_t launch_tiled(const GemmArgs& a) {
   }
   const dim3 grid(g.tiles_m * g.tiles_n, g.S);
   const hipError_t e = g.kind == TILE_LARGE      ? launch_act<LargeTile>(a, p, grid)
+                       : g.kg == 2                 ? launch_act<SmallTile2>(a, p, grid)
                        : g.kps >= kDeepBlocks      ? launch_act<SmallTileDeep>(a, p, grid)
                                                    : launch_act<SmallTile>(a, p, grid);
   if (e != hipSuccess || g.S == 1) return e;
