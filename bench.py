@@ -67,7 +67,7 @@ def algo_bytes(M, K, N, g, zeros, nf4=False, act_bytes=2, out_bytes=2):
 KERNEL_SOURCES = {
     # kernel family -> the sources that define its code and launch geometry
     "decode": lambda f: f.startswith("w4a16_decode"),
-    "tiled": lambda f: f == "w4a16_tiled.hip",
+    "tiled": lambda f: f.startswith("w4a16_tiled"),
     "skinny": lambda f: f == "w4a16_skinny.hip",
 }
 

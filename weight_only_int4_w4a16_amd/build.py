@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libw4a16.so")
 SOURCES = ["w4a16_api.hip", "w4a16_pack.hip", "w4a16_decode.hip", "w4a16_tiled.hip",
            "w4a16_skinny.hip", "w4a16_w4a8.hip", "w4a16_probe.hip"] + [
-    f"w4a16_decode_{a}_{f}.hip" for a in ("f16", "bf16") for f in ("asym", "sym", "nf4")]
+    f"w4a16_decode_{a}_{f}.hip" for a in ("f16", "bf16") for f in ("asym", "sym", "nf4")] + [
+    f"w4a16_tiled_{t}.hip" for t in ("large", "small", "smalldeep", "small2")]
 ARCH = os.environ.get("W4A16_ARCH", "gfx950")
 
 
@@ -37,17 +38,30 @@ def common_flags() -> list:
             f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 
 
-def _newest_header() -> float:
-    heads = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".h"))]
-    heads.append(os.path.join(ROOT, "include", "w4a16.h"))
-    return max(os.path.getmtime(h) for h in heads)
+def _header_deps(path: str, seen=None) -> set:
+    """The local headers a source includes, directly or through other headers."""
+    seen = set() if seen is None else seen
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line.startswith('#include "'):
+                continue
+            name = line.split('"')[1]
+            for d in (CSRC, os.path.join(ROOT, "include")):
+                h = os.path.join(d, name)
+                if os.path.exists(h) and h not in seen:
+                    seen.add(h)
+                    _header_deps(h, seen)
+                    break
+    return seen
 
 
 def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     if incremental and os.path.exists(obj):
         t = os.path.getmtime(obj)
-        if t > os.path.getmtime(os.path.join(CSRC, src)) and t > _newest_header():
+        deps = [os.path.join(CSRC, src), *_header_deps(os.path.join(CSRC, src))]
+        if all(t > os.path.getmtime(d) for d in deps):
             return obj
     cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

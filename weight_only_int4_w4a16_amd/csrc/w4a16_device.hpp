@@ -340,6 +340,29 @@ __device__ inline u4_t scale_act8(u4_t x, u4_t s) {
   return r;
 }
 
+// ---------------------------------------------------------------------------------------
+// Buffer loads. A buffer resource (gfx9 V#) holds a 64-bit base, no stride, num_records bytes
+// and a dword-3 word with a 32-bit data format, which untyped loads require. A load of
+// base + voffset + soffset whose offset lies at or past num_records returns zeros. The GEMM
+// kernels keep the per-lane part of every address in one VGPR (voffset) and advance the
+// per-block part in an SGPR (soffset), so their K loops spend no vector instructions on
+// addresses.
+// ---------------------------------------------------------------------------------------
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a voffset past every num_records used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+// 16 bytes per lane from global memory straight into LDS (buffer_load_dwordx4 ... lds): lane l
+// writes dst + 16 l (dst is the same for the whole wave)
+__device__ __forceinline__ void buffer_copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                     uint16_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)voff,
+                                           (int)soff, 0, 0);
+}
+
 // fp32 -> output element
 __device__ inline void store_out(void* out, size_t idx, float v, int out_dtype) {
   if (out_dtype == 2) {

@@ -26,6 +26,8 @@
 // column l%32 of a strip pair, k = 16t + 8(l/32) .. +8 at step t of a 128-k block. The codes of
 // those k are word t/2 of the packed chunk lane 16((2t + l/32) % 4) + l%16 owns (as in the
 // batched kernel). Each word is dequantized once per workgroup and used for MT row tiles.
+#include <type_traits>
+
 #include "w4a16_device.hpp"
 #include "w4a16_launch.hpp"
 
@@ -73,15 +75,6 @@ __device__ __forceinline__ void skinny_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Sixteen zero bytes in device memory: the source of the activation chunks past a ragged K.
-__device__ __attribute__((aligned(16))) const uint16_t kSkinnyZero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-
-// 16 bytes per lane from global memory straight into LDS: lane l writes dst + 16 l (dst is
-// the same for the whole wave)
-__device__ __forceinline__ void skinny_copy16(const uint16_t* src, uint16_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-
 // GLU: pair 0 holds two gate strips and pair 1 the matching up strips; the output is
 // h = SiLU(gate) * up, [M][N/2].
 template <int ACT, int GPC, int FMT, int MT, bool GLU>
@@ -122,53 +115,61 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_kernel(SkinnyParams 
 
   // activation copies: instruction j of a slot covers its rows 8j .. 8j+7, lane l row
   // 8j + l/8 and position l%8, which holds 16-byte chunk (l%8) ^ (row/2 % 8) of the row's half
-  // block (rows past M repeat row M-1 and are never stored)
-  const uint16_t* xsrc[KX];  // this lane's chunk of the slice's first half, per instruction
-  int xoff[KX];
+  // block (rows past M repeat row M-1 and are never stored). Offsets are bytes from the tile's
+  // first row and the slice's first k; each half block adds 128 bytes (a scalar offset).
+  // RAGGED (K not a multiple of 128) is decided once per launch, outside the K loop: a branch
+  // around the copies inside the loop would make the compiler lose count of the loads in
+  // flight and wait for every one of them before multiplying.
+  const int tile_rows = min(32 * MT, M - m0);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(p.x + (size_t)m0 * K, (uint32_t)tile_rows * K * 2);
+  uint32_t xoff[KX];
 #pragma unroll
   for (int j = 0; j < KX; ++j) {
     const int row = 8 * j + (lane >> 3);
-    xoff[j] = kc0 * 128 + ((lane & 7) ^ ((row >> 1) & 7)) * 8;
-    xsrc[j] = p.x + (size_t)min(m0 + row, M - 1) * K + xoff[j];
+    xoff[j] = (uint32_t)(min(row, tile_rows - 1) * K + kc0 * 128 + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2;
   }
-  auto load_x = [&](int h, int slot) __attribute__((always_inline)) {
-    const int kh = 64 * h;  // wave-uniform
-    if (kc0 * 128 + kh + 64 <= K) {  // the whole half lies below K
+  auto load_x = [&](int h, int slot, auto ragged) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < KX; ++j) skinny_copy16(xsrc[j] + kh, ring + slot * SLOT + j * 512);
-    } else {
-#pragma unroll
-      for (int j = 0; j < KX; ++j)
-        skinny_copy16(xoff[j] + kh < K ? xsrc[j] + kh : kSkinnyZero, ring + slot * SLOT + j * 512);
+    for (int j = 0; j < KX; ++j) {
+      uint32_t voff = xoff[j];
+      if constexpr (decltype(ragged)::value) {  // chunks past K read out of range: zeros
+        const int row = 8 * j + (lane >> 3);
+        const int k = kc0 * 128 + 64 * h + ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+        voff = k < K ? voff : kOutOfRange;
+      }
+      buffer_copy16_to_lds(xrs, voff, 128 * h, ring + slot * SLOT + j * 512);
     }
   };
 
   struct Codes {
     u4_t b[NP][2];          // chunks c0 and c0 + 32 of the lane's strip
-    uint16_t s[NP][GPC];    // scale (NF4: absmax)
+    uint32_t s[NP][GPC];    // scale (NF4: absmax), zero-extended by the load
     uint32_t z[NP][GPC];
   };
-  // per-lane bases; each load adds a wave-uniform offset
-  const u4_t* bsrc[NP];
-  const uint16_t* ssrc[NP];
-  const uint32_t* zsrc[NP];
+  // per-lane byte offsets from the first strip of the workgroup (codes), from the group's row
+  // (scales, zero-points); each load adds a wave-uniform offset
+  const int nbase = GLU ? min(2 * tn, p.half - 1) : min(tn * 2 * NP, p.NT - 1);  // lowest strip
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(p.packed + (size_t)nbase * KC * 64, 0xFFFFFFFFu);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.scales, (uint32_t)p.NG * N * 2);
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(ZEROS ? (const void*)p.qzeros : (const void*)p.scales, (uint32_t)p.NG * (N >> 3) * 4);
+  uint32_t boff[NP], soff[NP], zoff[NP];
 #pragma unroll
   for (int pr = 0; pr < NP; ++pr) {
-    bsrc[pr] = p.packed + (size_t)(col[pr] >> 4) * KC * 64 + c0;
-    ssrc[pr] = p.scales + col[pr];
-    zsrc[pr] = p.qzeros + (col[pr] >> 3);
+    boff[pr] = (uint32_t)(strip_of(pr) - nbase) * (uint32_t)KC * 1024u + (uint32_t)c0 * 16u;
+    soff[pr] = (uint32_t)col[pr] * 2u;
+    zoff[pr] = (uint32_t)(col[pr] >> 3) * 4u;
   }
+  constexpr int kNT = 2;  // aux bits: non-temporal (the codes are read once)
   auto load_b = [&](Codes& R, int kc) __attribute__((always_inline)) {
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
-      const u4_t* blk = bsrc[pr] + (size_t)kc * 64;
-      R.b[pr][0] = __builtin_nontemporal_load(blk);
-      R.b[pr][1] = __builtin_nontemporal_load(blk + 32);
+      R.b[pr][0] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[pr], kc * 1024, kNT));
+      R.b[pr][1] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[pr] + 512, kc * 1024, kNT));
 #pragma unroll
       for (int gi = 0; gi < GPC; ++gi) {
         const int g = min(kc * GPC + gi, p.NG - 1);  // groups past K are never used
-        R.s[pr][gi] = ssrc[pr][(size_t)g * N];
-        if constexpr (ZEROS) R.z[pr][gi] = zsrc[pr][(size_t)g * (N >> 3)];
+        R.s[pr][gi] = __builtin_amdgcn_raw_buffer_load_b16(srs, soff[pr], g * N * 2, 0);
+        if constexpr (ZEROS) R.z[pr][gi] = __builtin_amdgcn_raw_buffer_load_b32(zrs, zoff[pr], g * (N >> 3) * 4, 0);
       }
     }
   };
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_kernel(SkinnyParams 
   // instructions with no branch around them and the in-order load counter counts exactly:
   // after half h's copies come RA - 1 steps' copies and RA/2 code blocks. The prologue
   // interleaves its copies and code blocks so that the count holds from the first step.
-  if (nh > 0) {
+  auto k_loop = [&](auto ragged) __attribute__((always_inline)) {
     Codes R[RB];
     static_assert(RB == 4 && (RA == 4 || RA == 2), "the prologue order below");
     auto pro_b = [&](int j) __attribute__((always_inline)) {
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_kernel(SkinnyParams 
       __builtin_amdgcn_sched_barrier(0);
     };
     auto pro_x = [&](int q) __attribute__((always_inline)) {
-      load_x(min(q, nh - 1), q);
+      load_x(min(q, nh - 1), q, ragged);
       __builtin_amdgcn_sched_barrier(0);
     };
     if constexpr (RA == 4) {
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_kernel(SkinnyParams 
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int h = h0 + u;
-        load_x(min(h + RA - 1, nh - 1), (u + RA - 1) % RA);
+        load_x(min(h + RA - 1, nh - 1), (u + RA - 1) % RA, ragged);
         __builtin_amdgcn_sched_barrier(0);  // the count below assumes copies, then codes
         if (u % 2 == 0) load_b(R[(u / 2 + RB - 1) % RB], kc0 + min(h / 2 + RB - 1, nb - 1));
         __builtin_amdgcn_sched_barrier(0);
@@ -267,6 +268,12 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_kernel(SkinnyParams 
         if (h < nh) compute_half(R[(u / 2) % RB], u % 2, u % RA);
       }
     }
+  };
+  if (nh > 0) {
+    if (K % 128 == 0)
+      k_loop(std::false_type{});
+    else
+      k_loop(std::true_type{});
   }
 
   // ---- the W partial tiles, summed through LDS in wave order ----
