@@ -206,6 +206,13 @@ def test_kernel_name_and_strings(L):
     assert kernel_name(513, 2080, 44048, 32) == "w4a16_tiled_128x512"
     assert kernel_name(129, 4224, 28688, 64) == "w4a16_tiled_128x512_splitk"
     assert kernel_name(2048, 8192, 28672, 128) == "w4a16_tiled_128x512"
+    # the medium tile replaces the unsplit two-k-group small tile for groups of 32 or 64
+    # (NF4 blocks of 64 too) from 192 rows on, and only there
+    assert kernel_name(256, 4096, 14336, 128) == "w4a16_tiled_64x256_kg2"
+    assert kernel_name(256, 4096, 14336, 32) == "w4a16_tiled_128x128_kg2"
+    assert kernel_name(256, 4096, 14336, 64) == "w4a16_tiled_128x128_kg2"
+    assert kernel_name(128, 4096, 14336, 32) == "w4a16_tiled_64x256_kg2_splitk"
+    assert kernel_name(512, 4096, 14336, 32) == "w4a16_tiled_64x256"
     for s in range(5):
         assert L.w4a16_status_string(s)
     assert version()

@@ -129,6 +129,13 @@ SMALL = [
     (37, 640, 80, 64, "bf16", "sym"),
     (61, 4096, 48, 128, "f16", "sym"),
     (18, 2048, 8208, 128, "bf16", "nf4"),
+    # medium tile (128 x 128, two k-groups, one strip pair per wave): groups of 32 or 64 and
+    # NF4 from 192 rows on; a ragged last row tile, an odd block count split over the two
+    # k-groups, a ragged K
+    (200, 1024, 8192, 32, "f16", "asym"),
+    (256, 1152, 8192, 64, "f16", "nf4"),
+    (224, 640, 8192, 32, "bf16", "sym"),
+    (208, 1184, 8192, 32, "f16", "asym"),
 ]
 
 

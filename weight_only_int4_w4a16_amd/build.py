@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libw4a16.so")
 SOURCES = ["w4a16_api.hip", "w4a16_pack.hip", "w4a16_decode.hip", "w4a16_tiled.hip",
            "w4a16_skinny.hip", "w4a16_w4a8.hip", "w4a16_probe.hip"] + [
     f"w4a16_decode_{a}_{f}.hip" for a in ("f16", "bf16") for f in ("asym", "sym", "nf4")] + [
-    f"w4a16_tiled_{t}.hip" for t in ("large", "small", "smalldeep", "small2")]
+    f"w4a16_tiled_{t}.hip" for t in ("large", "small", "smalldeep", "small2", "med")]
 ARCH = os.environ.get("W4A16_ARCH", "gfx950")
 
 

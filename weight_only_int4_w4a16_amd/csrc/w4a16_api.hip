@@ -409,7 +409,7 @@ const char* w4a16_kernel_name(int M, int K, int N, int group_size) {
   GemmArgs a{};
   a.M = M; a.K = K; a.N = N; a.group_size = group_size;
   switch (choose_path(a)) {
-    case PATH_TILED: return w4a16::tiled_name(M, K, N);
+    case PATH_TILED: return w4a16::tiled_name(M, K, N, group_size);
     case PATH_SKINNY: return w4a16::skinny_name(M, K, N);
     default: return w4a16::decode_name(M, K, N, group_size, w4a16::ACT_F16);
   }

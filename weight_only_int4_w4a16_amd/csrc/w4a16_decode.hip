@@ -228,6 +228,7 @@ hipError_t launch_decode(const GemmArgs& a) {
     if (a.xscale && c.x_in_lds) {
       p.xscale = static_cast<const uint16_t*>(a.xscale);
     } else if (a.xscale) {  // x' to the workspace (launches run in order on the stream)
+      if (!a.workspace || a.workspace_bytes < (size_t)rows * a.K * 2) return hipErrorInvalidValue;
       const hipError_t e = launch_awq_scale(p.x, a.xscale, rows, a.K, a.act, a.workspace, a.stream);
       if (e != hipSuccess) return e;
       p.x = static_cast<const uint16_t*>(a.workspace);

@@ -75,7 +75,7 @@ hipError_t launch_awq_scale(const void* x, const void* s_inv, int rows, int K, i
 constexpr int kProbeSinkWords = 256;
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 const char* decode_name(int M, int K, int N, int group_size, int act);
-const char* tiled_name(int M, int K, int N);
+const char* tiled_name(int M, int K, int N, int group_size);
 bool tiled_supported(const GemmArgs& a);
 
 }  // namespace w4a16

@@ -381,6 +381,7 @@ hipError_t launch_skinny(const GemmArgs& a) {
   SkinnyParams p;
   p.x = static_cast<const uint16_t*>(a.x);
   if (a.xscale) {
+    if (!a.workspace || a.workspace_bytes < (size_t)a.M * a.K * 2) return hipErrorInvalidValue;
     const hipError_t e = launch_awq_scale(a.x, a.xscale, a.M, a.K, a.act, a.workspace, a.stream);
     if (e != hipSuccess) return e;
     p.x = static_cast<const uint16_t*>(a.workspace);

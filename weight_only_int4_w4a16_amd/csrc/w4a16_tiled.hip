@@ -13,6 +13,7 @@ W4A16_TILED_EXTERN(LargeTile)
 W4A16_TILED_EXTERN(SmallTile)
 W4A16_TILED_EXTERN(SmallTileDeep)
 W4A16_TILED_EXTERN(SmallTile2)
+W4A16_TILED_EXTERN(MedTile)
 }  // namespace tiled
 
 namespace {
@@ -66,7 +67,7 @@ int cu_count_tiled() {
   return v;
 }
 
-enum TileKind { TILE_LARGE = 0, TILE_SMALL = 1 };
+enum TileKind { TILE_LARGE = 0, TILE_SMALL = 1, TILE_MED = 2 };
 
 struct TiledGeometry {
   int kind;            // TileKind
@@ -82,8 +83,8 @@ TiledGeometry geometry_for(int M, int K, int N, int kind, int S, int kg) {
   g.kg = kg;
   const int KC = ceil_div(K, 128);
   g.kind = kind;
-  g.bm = kind == TILE_LARGE ? LargeTile::kBM : SmallTile::kBM;
-  g.bn = kind == TILE_LARGE ? LargeTile::kBN : SmallTile::kBN;
+  g.bm = kind == TILE_LARGE ? LargeTile::kBM : kind == TILE_MED ? MedTile::kBM : SmallTile::kBM;
+  g.bn = kind == TILE_LARGE ? LargeTile::kBN : kind == TILE_MED ? MedTile::kBN : SmallTile::kBN;
   g.tiles_m = ceil_div(M, g.bm);
   g.tiles_n = ceil_div(N, g.bn);
   g.kps = ceil_div(KC, S);
@@ -104,6 +105,7 @@ double modelled_us(const TiledGeometry& g, int M, int N, int cus) {
   const long per_cu = (wgs + cus - 1) / cus;
   const double wg_flops = 2.0 * g.bm * g.bn * g.kps * 128;
   const double rate = g.kind == TILE_LARGE ? 4.6e6
+                      : g.kind == TILE_MED   ? 4.6e6
                       : g.kg == 2            ? 4.0e6
                       : per_cu > 1           ? 3.4e6
                                              : 2.7e6;  // flop per us
@@ -132,6 +134,7 @@ int forced_tile() {
     if (!v) return -1;
     if (!strcmp(v, "large")) return (int)TILE_LARGE;
     if (!strcmp(v, "small")) return (int)TILE_SMALL;
+    if (!strcmp(v, "med")) return (int)TILE_MED;
     return -1;
   }();
   return forced;
@@ -143,21 +146,26 @@ int forced_tile() {
 // tracks the measured choices: large wins by 12-21% at 8192x28672 M=256, 28672x8192 M=256,
 // 8192x10240 M=512 and loses by 7-13% at 4096x4096 M=512 and 1024 (split-K partials
 // outweigh its rate); small matrices past 16 rows split K deeply (4096x4096 at M=17: S=16).
-TiledGeometry tiled_geometry(int M, int K, int N) {
+//
+// The choice depends on the shape only (never on the SwiGLU epilogue), so the workspace a
+// caller sizes for a shape is the workspace the launch uses.
+TiledGeometry tiled_geometry(int M, int K, int N, bool allow_forced = true) {
   const int cus = cu_count_tiled();
   const int KC = ceil_div(K, 128);
-  const int f = forced_tile(), fkg = forced_kg();
+  const int f = allow_forced ? forced_tile() : -1, fkg = allow_forced ? forced_kg() : 0;
   TiledGeometry best{};
   double best_us = -1;
-  for (int kind = 0; kind < 2; ++kind) {
+  for (int kind = 0; kind < 3; ++kind) {
     if (f >= 0 && kind != f) continue;
-    for (int kg = 1; kg <= (kind == TILE_SMALL ? 2 : 1); ++kg) {
+    if (kind == TILE_MED && f != TILE_MED) continue;
+    for (int kg = kind == TILE_MED ? 2 : 1; kg <= (kind == TILE_LARGE ? 1 : 2); ++kg) {
       if (fkg && kind == TILE_SMALL && kg != fkg) continue;
       for (int S = 1; S == 1 || KC / S >= 2 * kg; S *= 2) {
         const TiledGeometry g = geometry_for(M, K, N, kind, S, kg);
         const long wgs = (long)g.tiles_m * g.tiles_n * g.S;
         if (S > 1 && wgs > 4L * cus) break;
         if (kg == 2 && wgs > cus) break;  // two k-groups only where one workgroup per CU is left
+        if (kind == TILE_MED && S > 1) break;
         const double us = modelled_us(g, M, N, cus);
         if (best_us < 0 || us < best_us) {
           best = g;
@@ -166,15 +174,35 @@ TiledGeometry tiled_geometry(int M, int K, int N) {
       }
     }
   }
+  // a forced tile or k-group count with no valid launch for this shape: the model's choice
+  if (best_us < 0 && allow_forced) return tiled_geometry(M, K, N, false);
   return best;
+}
+
+// The tile a launch runs: the model's choice, with one swap that never changes the workspace
+// (both sides run with K unsplit). Where dequantization is dear (groups of 32 or 64 scale
+// pairs per block, or NF4's 16-level lookup, blocks of 64) and the model picks the small tile
+// with two k-groups and no K split, the medium tile, whose waves own 128 rows and feed each
+// dequantized word to twice the MFMAs, takes over from 192 rows on (4096x14336 at M=256:
+// g32 44.7 -> 41.4 us, NF4 54.0 -> 45.4 us; g128 41.6 -> 40.6 us, within run-to-run noise,
+// and M=128/192 slower, so those keep the small tile). The medium tile holds one strip pair
+// per wave, so a SwiGLU call keeps the small tile.
+TiledGeometry launch_geometry(int M, int K, int N, int group_size, bool glu) {
+  TiledGeometry g = tiled_geometry(M, K, N);
+  const bool forced_med = g.kind == TILE_MED;
+  if (glu && forced_med) return geometry_for(M, K, N, TILE_SMALL, 1, 2);
+  if (!glu && group_size <= 64 && M >= 192 && g.kind == TILE_SMALL && g.kg == 2 && g.S == 1)
+    return geometry_for(M, K, N, TILE_MED, 1, 2);
+  return g;
 }
 
 }  // namespace
 
 bool tiled_supported(const GemmArgs&) { return true; }
 
-const char* tiled_name(int M, int K, int N) {
-  const TiledGeometry g = tiled_geometry(M, K, N);
+const char* tiled_name(int M, int K, int N, int group_size) {
+  const TiledGeometry g = launch_geometry(M, K, N, group_size, false);
+  if (g.kind == TILE_MED) return "w4a16_tiled_128x128_kg2";
   if (g.kind == TILE_SMALL && g.kg == 2)
     return g.S > 1 ? "w4a16_tiled_64x256_kg2_splitk" : "w4a16_tiled_64x256_kg2";
   if (g.kind == TILE_SMALL) return g.S > 1 ? "w4a16_tiled_64x256_splitk" : "w4a16_tiled_64x256";
@@ -194,7 +222,10 @@ size_t tiled_workspace_bytes(int M, int K, int N) {
 }
 
 hipError_t launch_tiled(const GemmArgs& a) {
-  const TiledGeometry g = tiled_geometry(a.M, a.K, a.N);
+  const TiledGeometry g = launch_geometry(a.M, a.K, a.N, a.group_size, a.glu);
+  // never write past the caller's scratch: the split-K partials, then (AWQ) x'
+  const size_t need = (a.xscale ? align256(g.partial_bytes) + align256((size_t)a.M * a.K * 2) : g.partial_bytes);
+  if (need && (!a.workspace || a.workspace_bytes < need)) return hipErrorInvalidValue;
   TiledParams p;
   p.x = static_cast<const uint16_t*>(a.x);
   p.M = a.M;
@@ -223,6 +254,7 @@ hipError_t launch_tiled(const GemmArgs& a) {
   }
   const dim3 grid(g.tiles_m * g.tiles_n, g.S);
   const hipError_t e = g.kind == TILE_LARGE      ? launch_act<LargeTile>(a, p, grid)
+                       : g.kind == TILE_MED        ? launch_act<MedTile>(a, p, grid)
                        : g.kg == 2                 ? launch_act<SmallTile2>(a, p, grid)
                        : g.kps >= kDeepBlocks      ? launch_act<SmallTileDeep>(a, p, grid)
                                                    : launch_act<SmallTile>(a, p, grid);

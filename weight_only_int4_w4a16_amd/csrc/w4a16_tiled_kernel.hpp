@@ -95,6 +95,7 @@ typedef TileShape<4, 8, 2, 2> LargeTile;
 typedef TileShape<2, 4, 2, 2> SmallTile;
 typedef TileShape<2, 4, 2, 4> SmallTileDeep;
 typedef TileShape<2, 4, 2, 2, 2> SmallTile2;
+typedef TileShape<4, 4, 1, 2, 2> MedTile;
 constexpr int kDeepBlocks = 16;  // k-blocks per workgroup from which the small tile goes deep
 
 enum Fmt { FMT_ASYM = 0, FMT_SYM = 1, FMT_NF4 = 2 };
@@ -171,6 +172,14 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
   const int kg = wave_id / kWaves;              // this wave's k-group
   const int wave = wave_id - kg * kWaves;       // and its column role within the group
   uint16_t* const lds_a = lds + (size_t)kg * kStages * kBM * 128;  // the group's ring
+  // k-groups keep their own block pace: each synchronizes its four waves through a counter in
+  // LDS instead of the workgroup barrier, so the wave of one group that shares a SIMD with a
+  // wave of the other is not held at every block while the other finishes
+  __shared__ uint32_t kg_count[kKG];
+  if constexpr (kKG > 1) {
+    if (threadIdx.x < kKG) kg_count[threadIdx.x] = 0;
+    __syncthreads();
+  }
   const int tiles = p.tiles_m * p.tiles_n;
   const int t = tile_of(blockIdx.x, tiles);
   const int tm = t % p.tiles_m, tn = t / p.tiles_m;  // neighbours share weight columns
@@ -383,8 +392,21 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
       auto step_block = [&](const Regs& Rb, Regs& Rn, int i, int slot, bool live) __attribute__((always_inline)) {
         wait_vmcnt<0>();                          // block i's codes and copies landed
         __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no LDS access moves across the barrier
-        __builtin_amdgcn_s_barrier();             // every wave's copies of block i are in LDS, and
-                                                  // every wave is done with block i-1's slot
+        // every wave's copies of block i are in LDS, and every wave is done with block i-1's
+        // slot: the workgroup barrier, or with k-groups this group's count reaching 4 (i + 1)
+        // (LDS operations of a wave complete in order, so its count comes after its reads of
+        // block i-1, and after its copies of block i by the wait above). The wait is bounded,
+        // so a wave always ends.
+        if constexpr (kKG == 1) {
+          __builtin_amdgcn_s_barrier();
+        } else {
+          if (lane == 0) __hip_atomic_fetch_add(&kg_count[kg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          const uint32_t target = (uint32_t)kWaves * (uint32_t)(i + 1);
+          for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__hip_atomic_load(&kg_count[kg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_sched_barrier(0);
         const int kn = min(kb0 + i + 1, klast);
