@@ -476,16 +476,18 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
                 acc[mt][pr][e];
     }
     __syncthreads();
-    if (kg > 0) return;
+    if (GLU && kg > 0) return;
+    if (kg == 0) {
 #pragma unroll
-    for (int g = 1; g < kKG; ++g)
+      for (int g = 1; g < kKG; ++g)
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
+        for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-        for (int pr = 0; pr < kPairs; ++pr)
+          for (int pr = 0; pr < kPairs; ++pr)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            acc[mt][pr][e] += red[(size_t)((g - 1) * kWaves + wave) * kTile + ((mt * kPairs + pr) * 16 + e) * 64 + lane];
+            for (int e = 0; e < 16; ++e)
+              acc[mt][pr][e] += red[(size_t)((g - 1) * kWaves + wave) * kTile + ((mt * kPairs + pr) * 16 + e) * 64 + lane];
+    }
   }
 
   // ---- epilogue ----
@@ -511,24 +513,53 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
         }
     }
     return;
-  }
+  } else {
+    // The tile goes out in slices of 32 rows through LDS (over the rings): each lane writes its
+    // values of the slice, converted to the output type, at their row and column; then every
+    // thread stores whole 16-byte runs of rows. Written straight from the MFMA layout, a
+    // lane's values lie in one column, so the stores were 2 or 4 bytes each (measured: the
+    // output of 4096x14336 at M=256 took 6.5 us that way). K split: the slice's fp32 partials.
+    constexpr int kBN = T::kBN;
+    static_assert(32 * kBN * 4 <= T::kLdsBytes, "a 32-row slice of fp32 values fits in the rings");
+    const bool split = p.S > 1;
+    const int esz = split || p.out_dtype == 2 ? 4 : 2;  // bytes per stored element
+    char* const dst = split ? reinterpret_cast<char*>(p.partials + z * slice_stride) : static_cast<char*>(p.out);
+    char* const stage = reinterpret_cast<char*>(lds);
+    const int row_bytes = kBN * esz;
+    const int chunks_per_row = row_bytes / 16;
+    const int col0 = tn * kBN;
+    wait_vmcnt<0>();  // no copy (a re-read past the slice) is still landing in the rings
+    __syncthreads();  // every wave is done with the rings (and the k-groups' partial sums)
 #pragma unroll
-  for (int pr = 0; pr < kPairs; ++pr) {
-    const int nt = nt0 + 2 * pr + ((lane >> 4) & 1);
-    if (nt < p.NT) {
-      const int col = nt * 16 + (lane & 15);
+    for (int mt = 0; mt < kMT; ++mt) {
+      if (kg == 0) {
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
+        for (int pr = 0; pr < kPairs; ++pr) {
+          const int c = wave * kStrips * 16 + pr * 32 + (lane & 31);  // column in the tile
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = m0 + mt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (p.S == 1) {
-            if (m < M) store_out(p.out, (size_t)m * N + col, acc[mt][pr][i], p.out_dtype);
-          } else if (m < M) {
-            // K split: this slice's fp32 partial tile; the reduce kernel sums the slices
-            p.partials[z * slice_stride + (size_t)m * N + col] = acc[mt][pr][i];
+          for (int i = 0; i < 16; ++i) {
+            const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);  // row in the slice
+            const float v = acc[mt][pr][i];
+            char* const e = stage + r * row_bytes + c * esz;
+            if (esz == 4)
+              *reinterpret_cast<float*>(e) = v;
+            else if (p.out_dtype == 0)
+              *reinterpret_cast<_Float16*>(e) = (_Float16)v;
+            else
+              *reinterpret_cast<__bf16*>(e) = (__bf16)v;
           }
         }
+      }
+      __syncthreads();
+      for (int q = threadIdx.x; q < 32 * chunks_per_row; q += T::kThreads) {
+        const int rr = q / chunks_per_row, cc = q - rr * chunks_per_row;
+        const int m = m0 + mt * 32 + rr;
+        const int col = col0 + cc * (16 / esz);  // N is a multiple of 16: a run is all in or out
+        if (m < M && col < N)
+          *reinterpret_cast<u4_t*>(dst + ((size_t)m * N + col) * esz) =
+              *reinterpret_cast<const u4_t*>(stage + rr * row_bytes + cc * 16);
+      }
+      __syncthreads();
     }
   }
 }
