@@ -416,7 +416,11 @@ const char* w4a16_kernel_name(int M, int K, int N, int group_size) {
 }
 
 const char* w4a16_status_string(w4a16_status s) {
-  switch (s) {
+  // a C caller may pass any int: read it as one (loading an enum outside its enumerators'
+  // range is undefined in C++)
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case W4A16_OK: return "ok";
     case W4A16_ERR_ARG: return "invalid argument";
     case W4A16_ERR_UNSUPPORTED: return "unsupported shape";
