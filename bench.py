@@ -264,7 +264,10 @@ def sweep(args, torch, w4) -> int:
     gen = torch.Generator(device=dev)
     gen.manual_seed(20261203)
     codebook = None
+    picks = [c for c in (args.sweep_configs or "").split(",") if c]
     for name, fmt, g, act, shapes, Ms in SWEEP:
+        if picks and not any(c in name for c in picks):
+            continue
         tdt = torch.float16 if act == "f16" else torch.bfloat16
         nf4 = fmt == "nf4"
         for K, N in shapes:
@@ -551,6 +554,9 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="per-(config, shape, M) timing table of every benchmark config, one JSON "
                          "line per row, instead of the step benchmark")
+    ap.add_argument("--sweep-configs", default=None,
+                    help="--sweep: only the configs whose name contains one of these "
+                         "comma-separated strings (e.g. 'g32,nf4')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (x4), the known-size reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")

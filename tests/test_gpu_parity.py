@@ -104,6 +104,15 @@ SMALL = [
     (15, 2080, 12304, 32, "f16", "asym"),
     (12, 4096, 8208, 128, "f16", "sym"),
     (8, 4096, 16400, 32, "f16", "asym"),
+    # groups of 32 and 64 with four-block pipeline groups (one scale and zero word per block
+    # and strip, shared between the lanes of a column): waves with several groups, a ragged
+    # last group, two-strip SwiGLU-free tiles at g128 beside them
+    (1, 4096, 64, 32, "f16", "asym"),
+    (1, 6016, 48, 32, "bf16", "asym"),
+    (4, 8192, 48, 32, "f16", "sym"),
+    (2, 4096, 32, 64, "f16", "asym"),
+    (1, 2944, 64, 32, "f16", "nf4"),
+    (6, 4096, 80, 64, "bf16", "nf4"),
     # the smallest shapes: one 32-k step, one 16-column strip
     (1, 32, 16, 32, "f16", "asym"),
     (7, 64, 16, 64, "bf16", "sym"),

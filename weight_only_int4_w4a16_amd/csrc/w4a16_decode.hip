@@ -7,6 +7,15 @@
 
 namespace w4a16 {
 
+// The kernels are instantiated in the w4a16_decode_<act>_<fmt>.hip units, one per activation
+// type and weight format; declared here so this unit does not compile them all again.
+extern template hipError_t decode_dispatch<ACT_F16, FMT_ASYM>(const DecodeParams&, const DecodeConfig&, hipStream_t);
+extern template hipError_t decode_dispatch<ACT_F16, FMT_SYM>(const DecodeParams&, const DecodeConfig&, hipStream_t);
+extern template hipError_t decode_dispatch<ACT_F16, FMT_NF4>(const DecodeParams&, const DecodeConfig&, hipStream_t);
+extern template hipError_t decode_dispatch<ACT_BF16, FMT_ASYM>(const DecodeParams&, const DecodeConfig&, hipStream_t);
+extern template hipError_t decode_dispatch<ACT_BF16, FMT_SYM>(const DecodeParams&, const DecodeConfig&, hipStream_t);
+extern template hipError_t decode_dispatch<ACT_BF16, FMT_NF4>(const DecodeParams&, const DecodeConfig&, hipStream_t);
+
 namespace {
 
 int cu_count() {
