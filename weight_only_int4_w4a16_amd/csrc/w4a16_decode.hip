@@ -34,8 +34,9 @@ int cu_count() {
 constexpr size_t kXldsBytes = 128 * 1024;  // largest x staged in LDS per workgroup
 constexpr size_t kMaxLds = 160 * 1024;     // LDS per compute unit on gfx950
 
-// Launch geometry for a given tile width SW and wave count W per workgroup.
-DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
+// Launch geometry for a given tile width SW and wave count W per workgroup; `extra` LDS bytes
+// follow the activations (the fp16 NF4 pair table).
+DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W, size_t extra) {
   DecodeConfig c;
   c.KC = ceil_div(K, 128);
   c.NT = N / 16;
@@ -51,7 +52,7 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W) {
   c.W = ceil_div(c.KC, c.slice);  // drop waves left without blocks
   c.xstride = c.slice * 128 + 8;
   c.xslice = x_in_lds ? c.rows * c.xstride : 0;
-  c.lds_bytes = (size_t)c.W * SW * c.rows * 16 * 4 + (size_t)c.W * c.xslice * 2;
+  c.lds_bytes = (size_t)c.W * SW * c.rows * 16 * 4 + (size_t)c.W * c.xslice * 2 + (x_in_lds ? extra : 0);
   c.workspace_bytes = 0;
   return c;
 }
@@ -86,7 +87,7 @@ ForcedGeometry forced_geometry() {
   return f;
 }
 
-DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu,
+DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu, size_t extra,
                     bool allow_forced = true) {
   const int KC = ceil_div(K, 128), NT = N / 16;
   const ForcedGeometry fg = allow_forced ? forced_geometry() : ForcedGeometry{0, 0};
@@ -105,13 +106,13 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu
     for (int W = wmax; W >= 1; W >>= 1) {
       if (W > 1 && W > KC / D) continue;  // every wave streams at least one whole group
       if (fg.w && fg.w != W) continue;
-      DecodeConfig c = geometry(M, K, N, x_in_lds, SW, W);
+      DecodeConfig c = geometry(M, K, N, x_in_lds, SW, W, extra);
       // the same number of groups per wave with whole groups only, on fewer waves where the
       // slice would end in a partial group (14336 = 112 blocks: 14 waves of 8, not 16 of 7;
       // measured 9.6 -> 9.0 us at M=1)
       if (c.slice % D) {
         const int whole = ceil_div(c.slice, D) * D;
-        c = geometry(M, K, N, x_in_lds, SW, ceil_div(KC, whole));
+        c = geometry(M, K, N, x_in_lds, SW, ceil_div(KC, whole), extra);
       }
       c.glu = glu;
       if (c.lds_bytes > kMaxLds) continue;
@@ -147,7 +148,7 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu
     }
   }
   if (fg.sw) {  // a forced geometry as it is, or the unforced choice if it does not exist
-    return best_cost >= 0 ? best : choose(M, K, N, group_size, x_in_lds, glu, false);
+    return best_cost >= 0 ? best : choose(M, K, N, group_size, x_in_lds, glu, extra, false);
   }
   if (rows >= 8 && best_rounds > 1 && pbest_cost >= 0) return pbest;
   // One row of x: the waves of a tile stream four groups each where the tile allows it. The
@@ -159,7 +160,7 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu
   if (rows == 1 && x_in_lds) {
     const int D = decode_group_blocks(best.SW, GPC, x_in_lds);
     while (best.W * 2 <= wmax && ceil_div(ceil_div(KC, best.W * 2), D) >= 4) {
-      DecodeConfig c = geometry(M, K, N, x_in_lds, best.SW, best.W * 2);
+      DecodeConfig c = geometry(M, K, N, x_in_lds, best.SW, best.W * 2, extra);
       c.glu = glu;
       if (c.lds_bytes > kMaxLds) break;
       best = c;
@@ -172,14 +173,14 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu
 
 // x goes to LDS when it fits beside the reduction area; otherwise it is read per k-block
 // (every instantiated configuration exists for both activation types)
-DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu) {
+DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu, size_t extra_lds) {
   const int rows = M < 16 ? M : 16;
   const size_t xbytes = (size_t)rows * ceil_div(K, 128) * 128 * 2;
   if (xbytes <= kXldsBytes) {
-    const DecodeConfig c = choose(M, K, N, group_size, true, glu);
+    const DecodeConfig c = choose(M, K, N, group_size, true, glu, extra_lds);
     if (c.W > 0) return c;
   }
-  return choose(M, K, N, group_size, false, glu);
+  return choose(M, K, N, group_size, false, glu, 0);
 }
 
 namespace {
@@ -210,8 +211,8 @@ hipError_t launch_awq_scale(const void* x, const void* s_inv, int rows, int K, i
 
 // Rows of x one launch takes: at most 16, one MFMA tile (larger M goes to the batched
 // kernel; a caller of this launcher with more rows gets several launches).
-DecodeConfig decode_launch_config(int M, int K, int N, int group_size, bool glu) {
-  return decode_config(M < 16 ? M : 16, K, N, group_size, glu);
+DecodeConfig decode_launch_config(int M, int K, int N, int group_size, bool glu, size_t extra_lds = 0) {
+  return decode_config(M < 16 ? M : 16, K, N, group_size, glu, extra_lds);
 }
 
 const char* decode_name(int M, int K, int N, int group_size, int act) {
@@ -229,7 +230,9 @@ size_t decode_awq_workspace_bytes(int M, int K, int N, int group_size) {
 hipError_t launch_decode(const GemmArgs& a) {
   const size_t osz = a.out_dtype == 2 ? 4 : 2;
   for (int r0 = 0; r0 < a.M;) {
-    const DecodeConfig c = decode_launch_config(a.M - r0, a.K, a.N, a.group_size, a.glu);
+    // fp16 NF4 with x in LDS reads its levels from a pair table after x
+    const size_t extra = a.nf4 && a.act == ACT_F16 ? (size_t)kNf4PairEntries * 4 : 0;
+    const DecodeConfig c = decode_launch_config(a.M - r0, a.K, a.N, a.group_size, a.glu, extra);
     const int rows = c.rows;
     DecodeParams p;
     p.x = static_cast<const uint16_t*>(a.x) + (size_t)r0 * a.K;

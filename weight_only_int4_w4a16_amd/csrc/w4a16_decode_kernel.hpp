@@ -109,9 +109,10 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   constexpr int SPG = 4 / GPC;        // 32-k steps per scale group
   constexpr bool ZEROS = FMT == FMT_ASYM;
   constexpr bool DEFER = decode_defers_scale(ACT, FMT);
-  // fp16 NF4 with x in LDS: x is staged with each group of eight k in the packed nibble order,
-  // so the codebook levels go into the MFMA without regrouping
-  constexpr bool XNIB = XL && DEFER && FMT == FMT_NF4;
+  // fp16 NF4 with x in LDS: the levels come from the workgroup's pair table in LDS, two codes
+  // per read, in the word's byte order, and x is staged with each group of eight k in that
+  // order, so the levels go into the MFMA without regrouping
+  constexpr bool XPAIR = XL && DEFER && FMT == FMT_NF4;
 
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
@@ -129,6 +130,9 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   float* red = reinterpret_cast<float*>(lds);                                   // [W][SW][rows][16]
   uint16_t* xs = reinterpret_cast<uint16_t*>(red + (size_t)p.W * SW * rows * 16) +
                  (size_t)wave * p.xslice;                                        // [rows][xstride]
+  // XPAIR: the NF4 pair table after every wave's x (16-byte aligned: xslice is a multiple of 8)
+  uint32_t* const ptab = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(red + (size_t)p.W * SW * rows * 16) +
+                                                     (size_t)p.W * p.xslice);
 
   // ---- group loads: codes, per-group metadata and (not XL) the A fragments ----
   u4_t bA[D][SW], bB[D][SW];
@@ -176,7 +180,12 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
     for (int mt = 0; mt < MT; ++mt) acc[sw][mt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
   Nf4Lut lut;
-  if constexpr (FMT == FMT_NF4) lut = load_nf4_lut(p.codebook);
+  if constexpr (XPAIR) {
+    nf4_pair_table_fill(ptab, p.codebook);
+    __syncthreads();  // the table is complete before any wave reads it
+  } else if constexpr (FMT == FMT_NF4) {
+    lut = load_nf4_lut(p.codebook);
+  }
 
   // GUARD: the group may run past the wave's slice or end inside a ragged last k-block;
   // full groups take the branch-free copy
@@ -234,7 +243,9 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
               for (int sw = 0; sw < SW; ++sw) {
                 const uint32_t w = b[d][sw][j];
                 if constexpr (FMT == FMT_NF4) {
-                  const AT bq = XNIB ? nf4_levels_f16_nibble_order(w, lut) : nf4_levels_f16(w, lut);
+                  AT bq;
+                  if constexpr (XPAIR) bq = nf4_levels_f16_pairs(w, ptab);
+                  else bq = nf4_levels_f16(w, lut);
 #pragma unroll
                   for (int mt = 0; mt < MT; ++mt)
                     part[sw][mt] = mfma16(a[mt], bq, first ? f4_t{0.f, 0.f, 0.f, 0.f} : part[sw][mt]);
@@ -311,7 +322,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
       for (int i = 0; i < kXRegs; ++i) {
         u4_t v = xr[i];
         if constexpr (XS) v = scale_act8<ACT>(v, xsr[i]);
-        if constexpr (XNIB) v = act8_to_nibble_order(v);
+        if constexpr (XPAIR) v = act8_to_pair_order(v);
         *reinterpret_cast<u4_t*>(xs + xoff[i]) = v;
       }
       // chunks beyond the register-staged ones (slices of several rows)
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
         const int m = c / cpr, cc = c - (c / cpr) * cpr;
         u4_t v = *reinterpret_cast<const u4_t*>(p.x + (size_t)m * K + kbeg + cc * 8);
         if constexpr (XS) v = scale_act8<ACT>(v, *reinterpret_cast<const u4_t*>(p.xscale + kbeg + cc * 8));
-        if constexpr (XNIB) v = act8_to_nibble_order(v);
+        if constexpr (XPAIR) v = act8_to_pair_order(v);
         *reinterpret_cast<u4_t*>(xs + (size_t)m * p.xstride + cc * 8) = v;
       }
     }

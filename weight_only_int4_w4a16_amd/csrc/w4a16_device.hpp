@@ -226,20 +226,28 @@ __device__ inline h8_t nf4_levels_f16(uint32_t w, const Nf4Lut& L) {
   return __builtin_bit_cast(h8_t, u4_t{c01, c23, c45, c67});
 }
 
-// The same levels in the word's nibble order, k = 0, 4, 1, 5, 2, 6, 3, 7 (no regrouping):
-// for a kernel whose activations are stored in that order too (the products and their sum
-// over the eight k are unchanged).
-__device__ inline h8_t nf4_levels_f16_nibble_order(uint32_t w, const Nf4Lut& L) {
-  uint32_t c04, c15, c26, c37;
-  lut16_half(L, w & 0x0F0F0F0Fu, c04, c15);          // codes 0, 4, 1, 5
-  lut16_half(L, (w >> 4) & 0x0F0F0F0Fu, c26, c37);   // codes 2, 6, 3, 7
-  return __builtin_bit_cast(h8_t, u4_t{c04, c15, c26, c37});
+// NF4 level pairs keyed by one byte of a packed word (two codes): entry b holds the fp16
+// levels of codes b & 15 and b >> 4 as a half2, 256 entries (1 KiB) in LDS, filled once per
+// workgroup. A word then costs four LDS reads and their byte offsets instead of a 16-way
+// select per code in registers.
+constexpr int kNf4PairEntries = 256;
+__device__ inline void nf4_pair_table_fill(uint32_t* tab, const uint16_t* codebook) {
+  for (int i = threadIdx.x; i < kNf4PairEntries; i += blockDim.x)
+    tab[i] = (uint32_t)codebook[i & 15] | ((uint32_t)codebook[i >> 4] << 16);
 }
 
-// Eight 16-bit activations (k order) rearranged to k = 0, 4, 1, 5, 2, 6, 3, 7.
-__device__ inline u4_t act8_to_nibble_order(u4_t v) {
-  return u4_t{perm_b32(v[2], v[0], 0x05040100u), perm_b32(v[2], v[0], 0x07060302u),
-              perm_b32(v[3], v[1], 0x05040100u), perm_b32(v[3], v[1], 0x07060302u)};
+// The eight fp16 codebook levels of one packed word from the pair table, in the word's byte
+// order: byte b holds device nibbles 2b and 2b + 1, i.e. k = 0, 2, 4, 6, 1, 3, 5, 7 (the
+// kernel's activations are staged in that order too).
+__device__ inline h8_t nf4_levels_f16_pairs(uint32_t w, const uint32_t* tab) {
+  const u4_t r{tab[w & 0xFFu], tab[(w >> 8) & 0xFFu], tab[(w >> 16) & 0xFFu], tab[w >> 24]};
+  return __builtin_bit_cast(h8_t, r);
+}
+
+// Eight 16-bit activations (k order) rearranged to k = 0, 2, 4, 6, 1, 3, 5, 7.
+__device__ inline u4_t act8_to_pair_order(u4_t v) {
+  return u4_t{perm_b32(v[1], v[0], 0x05040100u), perm_b32(v[3], v[2], 0x05040100u),
+              perm_b32(v[1], v[0], 0x07060302u), perm_b32(v[3], v[2], 0x07060302u)};
 }
 
 __device__ inline h8_t dequant_word_nf4_f16(uint32_t w, const Nf4Lut& L, h2_t a2) {
