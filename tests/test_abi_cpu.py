@@ -151,7 +151,7 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     assert kernel_name(12, 8192, 57344, 128).startswith("w4a16_skinny")
     assert kernel_name(16, 28672, 8192, 128).startswith("w4a16_tiled")
     assert kernel_name(17, 2048, 4096, 128).startswith("w4a16_decode")     # K N < 2^24
-    # 17..128 rows: skinny up to 8192-deep K; at 17..32 rows for up to 512 column tiles, at
+    # 17..128 rows: skinny up to 8192-deep K; at 17..32 rows for up to 1024 column tiles, at
     # 33..128 rows within one launch round and (8192-deep) from 160 column tiles
     assert kernel_name(17, 4096, 4096, 128).startswith("w4a16_skinny")
     assert kernel_name(32, 4096, 4096, 128).startswith("w4a16_skinny")
@@ -162,7 +162,8 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     assert kernel_name(64, 8192, 10240, 128).startswith("w4a16_skinny")
     assert kernel_name(32, 8192, 8192, 128).startswith("w4a16_skinny")
     assert kernel_name(64, 8192, 8192, 128).startswith("w4a16_tiled")      # 128 tiles < 160
-    assert kernel_name(32, 8192, 57344, 128).startswith("w4a16_tiled")     # 896 tiles > 512
+    assert kernel_name(32, 8192, 57344, 128).startswith("w4a16_skinny")    # 896 tiles <= 1024
+    assert kernel_name(32, 8192, 73728, 128).startswith("w4a16_tiled")     # 1152 tiles > 1024
     assert kernel_name(17, 14336, 4096, 128).startswith("w4a16_tiled")     # deeper than 8192
     assert kernel_name(64, 4096, 14336, 128).startswith("w4a16_skinny")
     assert kernel_name(96, 4096, 14336, 128).startswith("w4a16_tiled")     # 448 workgroups

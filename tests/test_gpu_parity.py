@@ -138,6 +138,10 @@ SMALL = [
     (37, 640, 80, 64, "bf16", "sym"),
     (61, 4096, 48, 128, "f16", "sym"),
     (18, 2048, 8208, 128, "bf16", "nf4"),
+    # skinny kernel over several launch rounds: one k-block per wave (a slice shorter than a
+    # pass of the two-set pipeline), and waves without blocks beside a ragged column tile
+    (30, 1024, 20480, 64, "f16", "asym"),
+    (25, 1152, 16400, 32, "bf16", "sym"),
     # medium tile (128 x 128, two k-groups, one strip pair per wave): groups of 32 or 64 and
     # NF4 from 192 rows on; a ragged last row tile, an odd block count split over the two
     # k-groups, a ragged K

@@ -48,10 +48,9 @@ Path forced_path() {
 
 // M <= 16 runs the decode kernel (one 16-row MFMA tile). 17..32 rows run the skinny kernel
 // (K split across the eight waves of a workgroup, reduced in LDS) on weights at most 8192 deep
-// with enough 64-column tiles to fill the chip (N/64 >= 80 K/4096) but not so many that the
-// batched kernel's larger tiles win (N/64 <= 512); measured at M=24/32, e.g. 4096x14336
-// 20.9 -> 16.5 / 21.6 -> 17.6 us, 8192x10240 27.4 -> 23.6 / 28.9 -> 27.0 us against the
-// batched kernel. Weights of at most 2^24 elements keep the decode kernel up to 32 rows, in
+// with up to 1024 64-column tiles (four launch rounds); measured at M=32 against the batched
+// kernel, e.g. 4096x14336 12.8 against 21.7 us, 8192x57344 69.8 against 78.3 us (wider N is
+// unmeasured and stays on the batched kernel). Weights of at most 2^24 elements keep the decode kernel up to 32 rows, in
 // 16-row launches (their tiles cannot fill the chip otherwise: 4096x4096 at M=32 14.5 us). The
 // other shapes past 16 rows run the batched kernel (its 64x256 tiles with K split, or the
 // 128x512 tiles), e.g. 14336x4096 at M=32 23.1 us against 44.6 skinny. From 12 rows on, a large
@@ -74,9 +73,8 @@ int device_cus() {
 
 // Measured on MI355X (fp16 g128, 17..128 rows): the skinny kernel wins wherever its workgroups
 // (64 columns by 32 or 64 rows, all of K) stream at most 8192-deep K and fit in one launch
-// round, by 10-40% (4096x14336 at M=64: 19.1 against 25.5 us; 4096x4096 at M=128: 15.7
-// against 23.0 us); at 17-32 rows also in two rounds (8192x28672 at M=32: 44.7 against 49.4
-// us). At 33+ rows on 8192-deep K with fewer than 160 column tiles the batched kernel's split
+// round, by 10-40% (4096x14336 at M=64: 17.3 against 25.5 us; 4096x4096 at M=128: 15.7
+// against 23.0 us); at 17-32 rows also in up to four rounds (above). At 33+ rows on 8192-deep K with fewer than 160 column tiles the batched kernel's split
 // K wins (8192x8192 at M=64: 21.9 against 26.4 us), and so it does for deeper K and wider N.
 Path choose_path(const GemmArgs& a) {
   const Path f = forced_path();
@@ -87,7 +85,7 @@ Path choose_path(const GemmArgs& a) {
   if (a.M > 16) {
     if (a.M <= 32 && kn < (1LL << 24)) return PATH_DECODE;
     if (a.K > 8192) return PATH_TILED;
-    if (a.M <= 32) return col_tiles <= 512 ? PATH_SKINNY : PATH_TILED;
+    if (a.M <= 32) return col_tiles <= 1024 ? PATH_SKINNY : PATH_TILED;
     const long long wgs = col_tiles * ((a.M + 63) / 64);
     return wgs <= device_cus() && (a.K <= 4096 || col_tiles >= 160) ? PATH_SKINNY : PATH_TILED;
   }

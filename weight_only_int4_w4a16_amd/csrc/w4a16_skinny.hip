@@ -13,11 +13,15 @@
 // wave order (deterministic, no global partials, no second launch).
 //
 // Two load streams per wave, each sized for where it comes from.
-// - Codes (HBM): whole 16-byte chunks, two per lane per pair and block, into four register
-//   sets, so three blocks (12 KiB per wave) are in flight while one is multiplied.
+// - Codes (HBM): whole 16-byte chunks, two per lane per pair and block, into two register
+//   sets: the next block (4 KiB per wave) is in flight while one is multiplied. Deeper
+//   prefetch loses here: with three blocks ahead every wave has asked for most of its slice
+//   at once, the chip's requests arrive in no useful order, and a wave's first block waits
+//   behind all of them (4096x14336 at M=32: 15.6 us with three blocks ahead, 16.5 with two,
+//   12.8 with one). One block ahead is still about 7 MiB in flight across the chip.
 // - Activations (L2: every workgroup reads all of x): half blocks (32 MT rows x 64 k) copied
-//   from global memory straight into a per-wave LDS ring (global_load_lds_dwordx4, eight rows
-//   of 128 bytes per instruction, so every request is a whole cache line). Row r of a slot
+//   from global memory straight into a per-wave pair of LDS slots (global_load_lds_dwordx4,
+//   eight rows of 128 bytes per instruction, so every request is a whole cache line). Row r of a slot
 //   holds its eight 16-byte chunks at positions c ^ (r/2 % 8), so the fragment reads of
 //   sixteen consecutive rows fall in sixteen different bank groups. Only the wave that fills
 //   a slot reads it, so its own load counter orders the two and no barrier is needed.
@@ -60,9 +64,9 @@ struct SkinnyParams {
 
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyPairs = 2;
-constexpr int kCodeSets = 4;  // code register sets: the block multiplied and three in flight
-// activation slots (half blocks) per wave: 4 for one row tile, 2 for two (16 KiB either way)
-constexpr int skinny_slots(int MT) { return MT == 1 ? 4 : 2; }
+constexpr int kCodeSets = 2;  // code register sets: the block multiplied and the next in flight
+// activation slots (half blocks) per wave: the half multiplied and the next one in flight
+constexpr int skinny_slots(int MT) { (void)MT; return 2; }
 constexpr int skinny_slot_halves(int MT) { return 32 * MT * 64; }
 constexpr int skinny_ring_halves(int MT) { return skinny_slots(MT) * skinny_slot_halves(MT); }
 constexpr size_t skinny_lds_bytes(int MT) { return (size_t)kSkinnyWaves * skinny_ring_halves(MT) * 2; }
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_kernel(SkinnyParams 
   // interleaves its copies and code blocks so that the count holds from the first step.
   auto k_loop = [&](auto ragged) __attribute__((always_inline)) {
     Codes R[RB];
-    static_assert(RB == 4 && (RA == 4 || RA == 2), "the prologue order below");
+    static_assert(RB == 2 && RA == 2, "the prologue order below");
     auto pro_b = [&](int j) __attribute__((always_inline)) {
       load_b(R[j], kc0 + min(j, nb - 1));
       __builtin_amdgcn_sched_barrier(0);
@@ -248,11 +252,8 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_kernel(SkinnyParams 
       load_x(min(q, nh - 1), q, ragged);
       __builtin_amdgcn_sched_barrier(0);
     };
-    if constexpr (RA == 4) {
-      pro_b(0); pro_b(1); pro_x(0); pro_x(1); pro_b(2); pro_x(2);
-    } else {
-      pro_b(0); pro_b(1); pro_b(2); pro_x(0);
-    }
+    pro_b(0);
+    pro_x(0);
     const int passes = (nh + U - 1) / U;
     for (int ps = 0; ps < passes; ++ps) {
       const int h0 = ps * U;
