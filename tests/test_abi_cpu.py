@@ -166,8 +166,17 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     assert kernel_name(32, 8192, 73728, 128).startswith("w4a16_tiled")     # 1152 tiles > 1024
     assert kernel_name(17, 14336, 4096, 128).startswith("w4a16_tiled")     # deeper than 8192
     assert kernel_name(64, 4096, 14336, 128).startswith("w4a16_skinny")
-    assert kernel_name(96, 4096, 14336, 128).startswith("w4a16_tiled")     # 448 workgroups
-    assert kernel_name(129, 4096, 4096, 128).startswith("w4a16_tiled")
+    # 65..128 rows where 64-row tiles would take two rounds: 128-row tiles (K <= 4096)
+    assert kernel_name(96, 4096, 14336, 128) == "w4a16_skinny_128x64"     # 224 workgroups
+    assert kernel_name(128, 4096, 14336, 128) == "w4a16_skinny_128x64"
+    assert kernel_name(128, 8192, 14336, 128).startswith("w4a16_tiled")   # deeper than 4096
+    assert kernel_name(128, 4096, 4096, 128) == "w4a16_skinny_64x64"      # one round of 64 rows
+    # 129..256 rows: one round of 64-row tiles filling at least half the chip, K <= 4096
+    assert kernel_name(129, 4096, 4096, 128) == "w4a16_skinny_64x64"      # 192 workgroups
+    assert kernel_name(256, 4096, 4096, 128) == "w4a16_skinny_64x64"      # 256 workgroups
+    assert kernel_name(257, 4096, 4096, 128).startswith("w4a16_tiled")
+    assert kernel_name(200, 2048, 64, 128).startswith("w4a16_tiled")      # 4 workgroups
+    assert kernel_name(192, 4096, 14336, 128).startswith("w4a16_tiled")
 
 
 def test_nf4_requires_codebook(L):
@@ -212,7 +221,8 @@ def test_kernel_name_and_strings(L):
     assert kernel_name(256, 4096, 14336, 128) == "w4a16_tiled_64x256_kg2"
     assert kernel_name(256, 4096, 14336, 32) == "w4a16_tiled_128x128_kg2"
     assert kernel_name(256, 4096, 14336, 64) == "w4a16_tiled_128x128_kg2"
-    assert kernel_name(128, 4096, 14336, 32) == "w4a16_tiled_64x256_kg2_splitk"
+    assert kernel_name(192, 4096, 14336, 32) == "w4a16_tiled_128x128_kg2"
+    assert kernel_name(128, 4096, 14336, 32) == "w4a16_skinny_128x64"
     assert kernel_name(512, 4096, 14336, 32) == "w4a16_tiled_64x256"
     for s in range(5):
         assert L.w4a16_status_string(s)

@@ -142,6 +142,14 @@ SMALL = [
     # pass of the two-set pipeline), and waves without blocks beside a ragged column tile
     (30, 1024, 20480, 64, "f16", "asym"),
     (25, 1152, 16400, 32, "bf16", "sym"),
+    # skinny kernel with 128-row tiles (four waves, where 64-row tiles would need a second
+    # launch round): ragged M, a ragged K split 3/3/3/0 over the waves, every format
+    (96, 512, 8256, 128, "f16", "asym"),
+    (80, 1152, 8704, 32, "bf16", "sym"),
+    (128, 640, 8256, 64, "f16", "nf4"),
+    # skinny kernel past 128 rows (one round of 64-row tiles): a ragged last row tile
+    (160, 768, 3072, 128, "f16", "asym"),
+    (256, 1024, 4096, 64, "bf16", "nf4"),
     # medium tile (128 x 128, two k-groups, one strip pair per wave): groups of 32 or 64 and
     # NF4 from 192 rows on; a ragged last row tile, an odd block count split over the two
     # k-groups, a ragged K

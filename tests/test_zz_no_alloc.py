@@ -37,7 +37,7 @@ def test_static_scratch_matches_workspace_path_twice_shrinking():
     torch = torch_mod()
     # first a shape whose batched launch splits K (scratch in use), then a smaller one that
     # splits K too, then a decode shape that needs no scratch
-    shapes = [(130, 4096, 4096, 128, "f16"), (136, 2048, 512, 64, "bf16"), (3, 1024, 512, 32, "f16")]
+    shapes = [(130, 8192, 4096, 128, "f16"), (136, 2048, 512, 64, "bf16"), (3, 1024, 512, 32, "f16")]
     needs = [w4.workspace_bytes(M, K, N, g) for (M, K, N, g, _) in shapes]
     assert needs[0] > needs[1] > 0 and needs[2] == 0 and needs[0] <= LIMIT
     for (M, K, N, g, act), need in zip(shapes, needs):

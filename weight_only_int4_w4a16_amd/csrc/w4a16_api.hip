@@ -58,36 +58,36 @@ Path forced_path() {
 // workgroup re-reads x from L2 with each group) leaves the decode kernel: for the skinny kernel
 // when at most 8192 deep (8192x57344 at M=12: 103.6 decode, 90.3 batched, 83.2 us skinny), for
 // the batched kernel otherwise (28672x8192 at M=12: 50.1 decode, 44.8 us batched).
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
-  if (v == 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
-  }
-  return v;
-}
-
-// Measured on MI355X (fp16 g128, 17..128 rows): the skinny kernel wins wherever its workgroups
+// Measured on MI355X (fp16 g128, 17..256 rows): the skinny kernel wins wherever its workgroups
 // (64 columns by 32 or 64 rows, all of K) stream at most 8192-deep K and fit in one launch
-// round, by 10-40% (4096x14336 at M=64: 17.3 against 25.5 us; 4096x4096 at M=128: 15.7
-// against 23.0 us); at 17-32 rows also in up to four rounds (above). At 33+ rows on 8192-deep K with fewer than 160 column tiles the batched kernel's split
-// K wins (8192x8192 at M=64: 21.9 against 26.4 us), and so it does for deeper K and wider N.
+// round, by 10-40% (4096x14336 at M=64: 17.3 against 25.5 us; 4096x4096 at M=128: 14.2
+// against 23.0 us, at M=256: 16.7 against 26.3 us); at 17-32 rows also in up to four rounds
+// (above). Where 64-row tiles would take more than one round at 65-128 rows and K <= 4096, its
+// 128-row tiles (four waves, one per SIMD) still win (4096x14336 at M=96: 26.0 against 30.1 us,
+// M=128: 27.8 against 32.0 us; at M=192 and 256 they lose, 49.4 and 53.6 against 34.1 and
+// 39.6 us). Past 128 rows the skinny kernel keeps only launches of one round of 64-row tiles
+// that fill at least half the chip (smaller ones are unmeasured). At 33+ rows on 8192-deep K with fewer than 160 column tiles the batched kernel's
+// split K wins (8192x8192 at M=64: 21.9 against 26.4 us), and so it does for deeper K, wider N
+// and more rows.
 Path choose_path(const GemmArgs& a) {
   const Path f = forced_path();
   if (f != PATH_AUTO) return f;
   const long long kn = (long long)a.K * a.N;
   const long long col_tiles = (a.N + 63) / 64;
-  if (a.M > 128) return PATH_TILED;
+  if (a.M > 256) return PATH_TILED;
   if (a.M > 16) {
     if (a.M <= 32 && kn < (1LL << 24)) return PATH_DECODE;
     if (a.K > 8192) return PATH_TILED;
     if (a.M <= 32) return col_tiles <= 1024 ? PATH_SKINNY : PATH_TILED;
-    const long long wgs = col_tiles * ((a.M + 63) / 64);
-    return wgs <= device_cus() && (a.K <= 4096 || col_tiles >= 160) ? PATH_SKINNY : PATH_TILED;
+    const long long cus = w4a16::device_cu_count();
+    const long long wgs = col_tiles * ((a.M + 63) / 64);  // 64-row tiles
+    if (a.M <= 128) {
+      if (wgs <= cus && (a.K <= 4096 || col_tiles >= 160)) return PATH_SKINNY;
+      // 128-row tiles
+      return a.K <= 4096 && col_tiles * ((a.M + 127) / 128) <= cus ? PATH_SKINNY : PATH_TILED;
+    }
+    // 129..256 rows: one round of 64-row tiles that fills at least half the chip
+    return a.K <= 4096 && wgs <= cus && 2 * wgs > cus ? PATH_SKINNY : PATH_TILED;
   }
   if (a.M < 12 || kn < (1LL << 27)) return PATH_DECODE;
   if (w4a16::decode_config(a.M, a.K, a.N, a.group_size, a.glu).x_in_lds) return PATH_DECODE;

@@ -48,6 +48,20 @@ struct DecodeConfig {
 DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu, size_t extra_lds = 0);
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (cached per device; 256 if it cannot be read).
+inline int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+  }
+  return v;
+}
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 hipError_t launch_pack(const uint32_t* qweight, int K, int N, uint32_t* packed, hipStream_t s);

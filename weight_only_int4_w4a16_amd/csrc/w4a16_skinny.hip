@@ -30,6 +30,8 @@
 // column l%32 of a strip pair, k = 16t + 8(l/32) .. +8 at step t of a 128-k block. The codes of
 // those k are word t/2 of the packed chunk lane 16((2t + l/32) % 4) + l%16 owns (as in the
 // batched kernel). Each word is dequantized once per workgroup and used for MT row tiles.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "w4a16_device.hpp"
@@ -62,14 +64,16 @@ struct SkinnyParams {
   int half;         // GLU: strips per half of the fused gate+up weight (NT / 2)
 };
 
-constexpr int kSkinnyWaves = 8;
+// waves per workgroup: eight for one or two row tiles; four for four (128 rows: a wave's
+// accumulators fill the AGPRs of a SIMD, and four waves' activation slots fill the LDS)
+constexpr int skinny_waves(int MT) { return MT == 4 ? 4 : 8; }
 constexpr int kSkinnyPairs = 2;
 constexpr int kCodeSets = 2;  // code register sets: the block multiplied and the next in flight
 // activation slots (half blocks) per wave: the half multiplied and the next one in flight
 constexpr int skinny_slots(int MT) { (void)MT; return 2; }
 constexpr int skinny_slot_halves(int MT) { return 32 * MT * 64; }
 constexpr int skinny_ring_halves(int MT) { return skinny_slots(MT) * skinny_slot_halves(MT); }
-constexpr size_t skinny_lds_bytes(int MT) { return (size_t)kSkinnyWaves * skinny_ring_halves(MT) * 2; }
+constexpr size_t skinny_lds_bytes(int MT) { return (size_t)skinny_waves(MT) * skinny_ring_halves(MT) * 2; }
 
 // s_waitcnt with only the vector-memory counter bounded (gfx9 encoding: vmcnt bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
@@ -82,9 +86,9 @@ __device__ __forceinline__ void skinny_wait_vmcnt() {
 // GLU: pair 0 holds two gate strips and pair 1 the matching up strips; the output is
 // h = SiLU(gate) * up, [M][N/2].
 template <int ACT, int GPC, int FMT, int MT, bool GLU>
-__global__ __launch_bounds__(64 * kSkinnyWaves) void skinny_kernel(SkinnyParams p) {
+__global__ __launch_bounds__(64 * skinny_waves(MT)) void skinny_kernel(SkinnyParams p) {
   typedef typename ActT<ACT>::type AT;
-  constexpr int W = kSkinnyWaves, NP = kSkinnyPairs, RB = kCodeSets, RA = skinny_slots(MT);
+  constexpr int W = skinny_waves(MT), NP = kSkinnyPairs, RB = kCodeSets, RA = skinny_slots(MT);
   constexpr bool ZEROS = FMT == FMT_ASYM;
   constexpr int SLOT = skinny_slot_halves(MT);
   constexpr int RING = skinny_ring_halves(MT);
@@ -322,13 +326,27 @@ struct SkinnyGeometry {
   size_t lds_bytes;
 };
 
+// W4A16_SKINNY_MT=1|2|4 pins the row tiles per workgroup (for benchmarking one against
+// another); read once per process.
+int forced_skinny_mt() {
+  static const int forced = [] {
+    const char* v = getenv("W4A16_SKINNY_MT");
+    if (!v) return 0;
+    const int mt = atoi(v);
+    return mt == 1 || mt == 2 || mt == 4 ? mt : 0;
+  }();
+  return forced;
+}
+
 SkinnyGeometry skinny_geometry(int M, int K, int N, bool glu) {
   SkinnyGeometry g;
-  g.MT = M <= 32 ? 1 : 2;
   const int KC = ceil_div(K, 128);
   g.tiles_n = glu ? (N / 2) / 32 + ((N / 2) % 32 ? 1 : 0) : ceil_div(N, 32 * kSkinnyPairs);
+  // 64-row tiles up to 64 rows, and beyond where they fit one launch round; else 128-row tiles
+  g.MT = M <= 32 ? 1 : (M <= 64 || (long)g.tiles_n * ceil_div(M, 64) <= device_cu_count()) ? 2 : 4;
+  if (forced_skinny_mt()) g.MT = forced_skinny_mt();
   g.tiles_m = ceil_div(M, 32 * g.MT);
-  g.slice = ceil_div(KC, kSkinnyWaves);
+  g.slice = ceil_div(KC, skinny_waves(g.MT));
   g.lds_bytes = skinny_lds_bytes(g.MT);
   return g;
 }
@@ -336,7 +354,7 @@ SkinnyGeometry skinny_geometry(int M, int K, int N, bool glu) {
 template <int ACT, int GPC, int FMT, int MT, bool GLU>
 hipError_t launch_cfg(const SkinnyParams& p, const SkinnyGeometry& g, hipStream_t s) {
   hipLaunchKernelGGL((skinny_kernel<ACT, GPC, FMT, MT, GLU>), dim3(g.tiles_n, g.tiles_m),
-                     dim3(64 * kSkinnyWaves), g.lds_bytes, s, p);
+                     dim3(64 * skinny_waves(MT)), g.lds_bytes, s, p);
   return hipGetLastError();
 }
 
@@ -344,7 +362,9 @@ template <int ACT, int GPC, int FMT>
 hipError_t launch_mt(const GemmArgs& a, const SkinnyParams& p, const SkinnyGeometry& g) {
   if (g.MT == 1)
     return a.glu ? launch_cfg<ACT, GPC, FMT, 1, true>(p, g, a.stream) : launch_cfg<ACT, GPC, FMT, 1, false>(p, g, a.stream);
-  return a.glu ? launch_cfg<ACT, GPC, FMT, 2, true>(p, g, a.stream) : launch_cfg<ACT, GPC, FMT, 2, false>(p, g, a.stream);
+  if (g.MT == 2)
+    return a.glu ? launch_cfg<ACT, GPC, FMT, 2, true>(p, g, a.stream) : launch_cfg<ACT, GPC, FMT, 2, false>(p, g, a.stream);
+  return a.glu ? launch_cfg<ACT, GPC, FMT, 4, true>(p, g, a.stream) : launch_cfg<ACT, GPC, FMT, 4, false>(p, g, a.stream);
 }
 
 template <int ACT, int GPC>
@@ -367,7 +387,7 @@ hipError_t launch_gpc(const GemmArgs& a, const SkinnyParams& p, const SkinnyGeom
 
 const char* skinny_name(int M, int K, int N) {
   const SkinnyGeometry g = skinny_geometry(M, K, N, false);
-  return g.MT == 1 ? "w4a16_skinny_32x64" : "w4a16_skinny_64x64";
+  return g.MT == 1 ? "w4a16_skinny_32x64" : g.MT == 2 ? "w4a16_skinny_64x64" : "w4a16_skinny_128x64";
 }
 
 // AWQ-scaled activations are not scaled in this kernel: the caller passes x' from the
