@@ -244,6 +244,41 @@ __device__ inline h8_t nf4_levels_f16_pairs(uint32_t w, const uint32_t* tab) {
   return __builtin_bit_cast(h8_t, r);
 }
 
+// The same eight levels in k order (four byte permutes on the pair-order words).
+__device__ inline u4_t nf4_levels_k_order(uint32_t w, const uint32_t* tab) {
+  const uint32_t p0 = tab[w & 0xFFu], p1 = tab[(w >> 8) & 0xFFu];     // (c0, c2), (c4, c6)
+  const uint32_t p2 = tab[(w >> 16) & 0xFFu], p3 = tab[w >> 24];      // (c1, c3), (c5, c7)
+  return u4_t{perm_b32(p2, p0, 0x05040100u), perm_b32(p2, p0, 0x07060302u),
+              perm_b32(p3, p1, 0x05040100u), perm_b32(p3, p1, 0x07060302u)};
+}
+
+// W_hat = RN_t(c[q] * a) for one packed word, levels from the pair table (the same values as
+// dequant_word_nf4_f16 / _bf16, which select them in registers).
+__device__ inline h8_t dequant_word_nf4_f16_tab(uint32_t w, const uint32_t* tab, h2_t a2) {
+  const u4_t c = nf4_levels_k_order(w, tab);
+  h8_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const h2_t d = as_h2(c[p]) * a2;
+    r[2 * p] = d[0];
+    r[2 * p + 1] = d[1];
+  }
+  return r;
+}
+
+__device__ inline b8_t dequant_word_nf4_bf16_tab(uint32_t w, const uint32_t* tab, float a) {
+  const u4_t c = nf4_levels_k_order(w, tab);
+  b8_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const h2_t h = as_h2(c[p]);
+    // fp16 level * fp16 absmax: exact in fp32 (11 x 11 significant bits); one rounding
+    r[2 * p] = (__bf16)((float)h[0] * a);
+    r[2 * p + 1] = (__bf16)((float)h[1] * a);
+  }
+  return r;
+}
+
 // Eight 16-bit activations (k order) rearranged to k = 0, 2, 4, 6, 1, 3, 5, 7.
 __device__ inline u4_t act8_to_pair_order(u4_t v) {
   return u4_t{perm_b32(v[1], v[0], 0x05040100u), perm_b32(v[3], v[2], 0x05040100u),

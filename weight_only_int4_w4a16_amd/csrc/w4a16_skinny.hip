@@ -73,7 +73,10 @@ constexpr int kCodeSets = 2;  // code register sets: the block multiplied and th
 constexpr int skinny_slots(int MT) { (void)MT; return 2; }
 constexpr int skinny_slot_halves(int MT) { return 32 * MT * 64; }
 constexpr int skinny_ring_halves(int MT) { return skinny_slots(MT) * skinny_slot_halves(MT); }
-constexpr size_t skinny_lds_bytes(int MT) { return (size_t)skinny_waves(MT) * skinny_ring_halves(MT) * 2; }
+// the waves' activation slots, then the NF4 level-pair table (1 KiB, filled for NF4 only)
+constexpr size_t skinny_lds_bytes(int MT) {
+  return (size_t)skinny_waves(MT) * skinny_ring_halves(MT) * 2 + kNf4PairEntries * 4;
+}
 
 // s_waitcnt with only the vector-memory counter bounded (gfx9 encoding: vmcnt bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
@@ -182,8 +185,12 @@ __global__ __launch_bounds__(64 * skinny_waves(MT)) void skinny_kernel(SkinnyPar
     }
   };
 
-  Nf4Lut lut;
-  if constexpr (FMT == FMT_NF4) lut = load_nf4_lut(p.codebook);
+  // NF4: the level-pair table after every wave's slots, complete before any wave reads it
+  uint32_t* const ptab = reinterpret_cast<uint32_t*>(lds + (size_t)W * RING);
+  if constexpr (FMT == FMT_NF4) {
+    nf4_pair_table_fill(ptab, p.codebook);
+    __syncthreads();
+  }
 
   f16v_t acc[MT][NP];
 #pragma unroll
@@ -219,9 +226,9 @@ __global__ __launch_bounds__(64 * skinny_waves(MT)) void skinny_kernel(SkinnyPar
         const uint32_t sraw = R.s[pr][gi];
         if constexpr (FMT == FMT_NF4) {
           if constexpr (ACT == ACT_F16)
-            bf[pr] = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
+            bf[pr] = dequant_word_nf4_f16_tab(w, ptab, as_h2(sraw * 0x00010001u));
           else
-            bf[pr] = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
+            bf[pr] = dequant_word_nf4_bf16_tab(w, ptab, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
         } else {
           const uint32_t zq = ZEROS ? (R.z[pr][gi] >> shift) & 0xFu : 8u;
           if constexpr (ACT == ACT_F16)
