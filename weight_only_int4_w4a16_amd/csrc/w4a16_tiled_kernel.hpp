@@ -277,8 +277,13 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  Nf4Lut lut;
-  if constexpr (FMT == FMT_NF4) lut = load_nf4_lut(p.codebook);
+  // NF4: the level-pair table after the rings (the launch adds its 1 KiB to the LDS size),
+  // complete before any wave reads it
+  const uint32_t* const ptab = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lds) + T::kLdsBytes);
+  if constexpr (FMT == FMT_NF4) {
+    nf4_pair_table_fill(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + T::kLdsBytes), p.codebook);
+    __syncthreads();
+  }
 
   f16v_t acc[kMT][kPairs];
 #pragma unroll
@@ -298,9 +303,9 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
       const uint32_t sraw = R.s[pr][gi];
       if constexpr (FMT == FMT_NF4) {
         if constexpr (ACT == ACT_F16)
-          bf[pr] = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
+          bf[pr] = dequant_word_nf4_f16_tab(w, ptab, as_h2(sraw * 0x00010001u));
         else
-          bf[pr] = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
+          bf[pr] = dequant_word_nf4_bf16_tab(w, ptab, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
       } else {
         const uint32_t zq = ZEROS ? (R.z[pr][gi] >> shift) & 0xFu : 8u;
         if constexpr (ACT == ACT_F16)
@@ -567,7 +572,8 @@ __global__ __launch_bounds__(T::kThreads) void tiled_kernel(TiledParams p) {
 template <int ACT, int GPC, class T, bool GLU>
 hipError_t launch_glu(const GemmArgs& a, const TiledParams& p, dim3 grid) {
   if (a.nf4)
-    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
+    hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_NF4, T, GLU>), grid, dim3(T::kThreads),
+                       T::kLdsBytes + kNf4PairEntries * 4, a.stream, p);
   else if (a.qzeros)
     hipLaunchKernelGGL((tiled_kernel<ACT, GPC, FMT_ASYM, T, GLU>), grid, dim3(T::kThreads), T::kLdsBytes, a.stream, p);
   else
