@@ -35,7 +35,7 @@ constexpr size_t kXldsBytes = 128 * 1024;  // largest x staged in LDS per workgr
 constexpr size_t kMaxLds = 160 * 1024;     // LDS per compute unit on gfx950
 
 // Launch geometry for a given tile width SW and wave count W per workgroup; `extra` LDS bytes
-// follow the activations (the fp16 NF4 pair table).
+// follow the activations (the NF4 level-pair table).
 DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W, size_t extra) {
   DecodeConfig c;
   c.KC = ceil_div(K, 128);
@@ -52,7 +52,7 @@ DecodeConfig geometry(int M, int K, int N, bool x_in_lds, int SW, int W, size_t 
   c.W = ceil_div(c.KC, c.slice);  // drop waves left without blocks
   c.xstride = c.slice * 128 + 8;
   c.xslice = x_in_lds ? c.rows * c.xstride : 0;
-  c.lds_bytes = (size_t)c.W * SW * c.rows * 16 * 4 + (size_t)c.W * c.xslice * 2 + (x_in_lds ? extra : 0);
+  c.lds_bytes = (size_t)c.W * SW * c.rows * 16 * 4 + (size_t)c.W * c.xslice * 2 + extra;
   c.workspace_bytes = 0;
   return c;
 }
@@ -180,7 +180,7 @@ DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu, size_t
     const DecodeConfig c = choose(M, K, N, group_size, true, glu, extra_lds);
     if (c.W > 0) return c;
   }
-  return choose(M, K, N, group_size, false, glu, 0);
+  return choose(M, K, N, group_size, false, glu, extra_lds);
 }
 
 namespace {
@@ -230,8 +230,8 @@ size_t decode_awq_workspace_bytes(int M, int K, int N, int group_size) {
 hipError_t launch_decode(const GemmArgs& a) {
   const size_t osz = a.out_dtype == 2 ? 4 : 2;
   for (int r0 = 0; r0 < a.M;) {
-    // fp16 NF4 with x in LDS reads its levels from a pair table after x
-    const size_t extra = a.nf4 && a.act == ACT_F16 ? (size_t)kNf4PairEntries * 4 : 0;
+    // NF4 reads its levels from a pair table after x
+    const size_t extra = a.nf4 ? (size_t)kNf4PairEntries * 4 : 0;
     const DecodeConfig c = decode_launch_config(a.M - r0, a.K, a.N, a.group_size, a.glu, extra);
     const int rows = c.rows;
     DecodeParams p;

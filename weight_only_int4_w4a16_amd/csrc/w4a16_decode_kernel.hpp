@@ -130,7 +130,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
   float* red = reinterpret_cast<float*>(lds);                                   // [W][SW][rows][16]
   uint16_t* xs = reinterpret_cast<uint16_t*>(red + (size_t)p.W * SW * rows * 16) +
                  (size_t)wave * p.xslice;                                        // [rows][xstride]
-  // XPAIR: the NF4 pair table after every wave's x (16-byte aligned: xslice is a multiple of 8)
+  // NF4: the level-pair table after every wave's x (16-byte aligned: xslice is a multiple of 8)
   uint32_t* const ptab = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(red + (size_t)p.W * SW * rows * 16) +
                                                      (size_t)p.W * p.xslice);
 
@@ -179,12 +179,9 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[sw][mt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-  Nf4Lut lut;
-  if constexpr (XPAIR) {
+  if constexpr (FMT == FMT_NF4) {
     nf4_pair_table_fill(ptab, p.codebook);
     __syncthreads();  // the table is complete before any wave reads it
-  } else if constexpr (FMT == FMT_NF4) {
-    lut = load_nf4_lut(p.codebook);
   }
 
   // GUARD: the group may run past the wave's slice or end inside a ragged last k-block;
@@ -222,9 +219,9 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
                 AT bf;
                 if constexpr (FMT == FMT_NF4) {
                   if constexpr (ACT == ACT_F16)
-                    bf = dequant_word_nf4_f16(w, lut, as_h2(sraw * 0x00010001u));
+                    bf = dequant_word_nf4_f16_tab(w, ptab, as_h2(sraw * 0x00010001u));
                   else
-                    bf = dequant_word_nf4_bf16(w, lut, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
+                    bf = dequant_word_nf4_bf16_tab(w, ptab, (float)__builtin_bit_cast(_Float16, (uint16_t)sraw));
                 } else {
                   const uint32_t zq = ZEROS ? (z[d][sw][gi] >> shift) & 0xFu : 8u;
                   if constexpr (ACT == ACT_F16)
@@ -245,7 +242,7 @@ __global__ __launch_bounds__(LB) void decode_kernel(DecodeParams p) {
                 if constexpr (FMT == FMT_NF4) {
                   AT bq;
                   if constexpr (XPAIR) bq = nf4_levels_f16_pairs(w, ptab);
-                  else bq = nf4_levels_f16(w, lut);
+                  else bq = __builtin_bit_cast(h8_t, nf4_levels_k_order(w, ptab));
 #pragma unroll
                   for (int mt = 0; mt < MT; ++mt)
                     part[sw][mt] = mfma16(a[mt], bq, first ? f4_t{0.f, 0.f, 0.f, 0.f} : part[sw][mt]);

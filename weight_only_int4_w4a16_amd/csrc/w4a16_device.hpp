@@ -183,53 +183,17 @@ __device__ inline b8_t dequant_word_bf16(uint32_t w, ZeroF32 zs) {
 }
 
 // ---------------------------------------------------------------------------------------
-// NF4 dequantization: W_hat = RN_t(c[q] * a). The 16 fp16 levels live in registers as
-// two byte tables (low and high bytes of each level); v_perm_b32 looks up four codes at
-// once from eight bytes, a bit-3 select picks the half of the table.
+// NF4 dequantization: W_hat = RN_t(c[q] * a), with the 16 fp16 levels c a kernel argument.
 // ---------------------------------------------------------------------------------------
-struct Nf4Lut {
-  uint32_t lo[4];  // low bytes of levels 0..15, four per word
-  uint32_t hi[4];  // high bytes
-};
-
 __device__ inline uint32_t perm_b32(uint32_t hi_word, uint32_t lo_word, uint32_t sel) {
   return __builtin_amdgcn_perm(hi_word, lo_word, sel);
-}
-
-// idx: four byte-lane indices 0..15 -> four table bytes
-__device__ inline uint32_t lut16_bytes(const uint32_t t[4], uint32_t idx) {
-  const uint32_t sel = idx & 0x07070707u;
-  const uint32_t a = perm_b32(t[1], t[0], sel);          // entries 0..7
-  const uint32_t b = perm_b32(t[3], t[2], sel);          // entries 8..15
-  const uint32_t m = ((idx >> 3) & 0x01010101u) * 0xFFu;  // 0xFF where idx >= 8
-  return (a & ~m) | (b & m);
-}
-
-// four codes (one per byte of idx) -> two half2 words holding levels (b0,b1), (b2,b3)
-__device__ inline void lut16_half(const Nf4Lut& L, uint32_t idx, uint32_t& h01, uint32_t& h23) {
-  const uint32_t lo = lut16_bytes(L.lo, idx);
-  const uint32_t hi = lut16_bytes(L.hi, idx);
-  h01 = perm_b32(hi, lo, 0x05010400u);  // bytes: lo0, hi0, lo1, hi1
-  h23 = perm_b32(hi, lo, 0x07030602u);  // bytes: lo2, hi2, lo3, hi3
-}
-
-// The eight fp16 codebook levels of one packed word, in k order (no absmax): the operand of
-// the fp16 decode kernel, which applies the absmax to each block's fp32 partial sum.
-__device__ inline h8_t nf4_levels_f16(uint32_t w, const Nf4Lut& L) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  const uint32_t i0 = perm_b32(hi, lo, 0x06040200u);  // codes 0,1,2,3
-  const uint32_t i1 = perm_b32(hi, lo, 0x07050301u);  // codes 4,5,6,7
-  uint32_t c01, c23, c45, c67;
-  lut16_half(L, i0, c01, c23);
-  lut16_half(L, i1, c45, c67);
-  return __builtin_bit_cast(h8_t, u4_t{c01, c23, c45, c67});
 }
 
 // NF4 level pairs keyed by one byte of a packed word (two codes): entry b holds the fp16
 // levels of codes b & 15 and b >> 4 as a half2, 256 entries (1 KiB) in LDS, filled once per
 // workgroup. A word then costs four LDS reads and their byte offsets instead of a 16-way
-// select per code in registers.
+// select per code in registers (two byte tables through v_perm_b32 and a select on code bit
+// 3, about 27 operations per word).
 constexpr int kNf4PairEntries = 256;
 __device__ inline void nf4_pair_table_fill(uint32_t* tab, const uint16_t* codebook) {
   for (int i = threadIdx.x; i < kNf4PairEntries; i += blockDim.x)
@@ -252,8 +216,8 @@ __device__ inline u4_t nf4_levels_k_order(uint32_t w, const uint32_t* tab) {
               perm_b32(p3, p1, 0x05040100u), perm_b32(p3, p1, 0x07060302u)};
 }
 
-// W_hat = RN_t(c[q] * a) for one packed word, levels from the pair table (the same values as
-// dequant_word_nf4_f16 / _bf16, which select them in registers).
+// W_hat = RN_t(c[q] * a) for one packed word, levels from the pair table: the level times the
+// absmax is exact in fp32 (11 x 11 significant bits), so the product rounds once.
 __device__ inline h8_t dequant_word_nf4_f16_tab(uint32_t w, const uint32_t* tab, h2_t a2) {
   const u4_t c = nf4_levels_k_order(w, tab);
   h8_t r;
@@ -283,61 +247,6 @@ __device__ inline b8_t dequant_word_nf4_bf16_tab(uint32_t w, const uint32_t* tab
 __device__ inline u4_t act8_to_pair_order(u4_t v) {
   return u4_t{perm_b32(v[1], v[0], 0x05040100u), perm_b32(v[3], v[2], 0x05040100u),
               perm_b32(v[1], v[0], 0x07060302u), perm_b32(v[3], v[2], 0x07060302u)};
-}
-
-__device__ inline h8_t dequant_word_nf4_f16(uint32_t w, const Nf4Lut& L, h2_t a2) {
-  // lo bytes: codes 0,4,1,5 ; hi bytes: codes 2,6,3,7 -> regroup to (0,1),(2,3),(4,5),(6,7)
-  const uint32_t lo = w & 0x0F0F0F0Fu;
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  const uint32_t i0 = perm_b32(hi, lo, 0x06040200u);  // codes 0,1,2,3
-  const uint32_t i1 = perm_b32(hi, lo, 0x07050301u);  // codes 4,5,6,7
-  uint32_t c01, c23, c45, c67;
-  lut16_half(L, i0, c01, c23);
-  lut16_half(L, i1, c45, c67);
-  const h2_t d0 = as_h2(c01) * a2;
-  const h2_t d1 = as_h2(c23) * a2;
-  const h2_t d2 = as_h2(c45) * a2;
-  const h2_t d3 = as_h2(c67) * a2;
-  h8_t r;
-  r[0] = d0[0]; r[1] = d0[1]; r[2] = d1[0]; r[3] = d1[1];
-  r[4] = d2[0]; r[5] = d2[1]; r[6] = d3[0]; r[7] = d3[1];
-  return r;
-}
-
-__device__ inline b8_t dequant_word_nf4_bf16(uint32_t w, const Nf4Lut& L, float a) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  const uint32_t i0 = perm_b32(hi, lo, 0x06040200u);
-  const uint32_t i1 = perm_b32(hi, lo, 0x07050301u);
-  uint32_t c[4];
-  lut16_half(L, i0, c[0], c[1]);
-  lut16_half(L, i1, c[2], c[3]);
-  b8_t r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const h2_t h = as_h2(c[p]);
-    // fp16 level * fp16 absmax: exact in fp32 (11 x 11 significant bits); one rounding
-    r[2 * p] = (__bf16)((float)h[0] * a);
-    r[2 * p + 1] = (__bf16)((float)h[1] * a);
-  }
-  return r;
-}
-
-__device__ inline Nf4Lut load_nf4_lut(const uint16_t* codebook) {
-  Nf4Lut L;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t v = codebook[4 * w + b];
-      lo |= (v & 0xFFu) << (8 * b);
-      hi |= (v >> 8) << (8 * b);
-    }
-    L.lo[w] = lo;
-    L.hi[w] = hi;
-  }
-  return L;
 }
 
 // ---------------------------------------------------------------------------------------

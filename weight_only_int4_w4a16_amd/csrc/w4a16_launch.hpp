@@ -44,7 +44,7 @@ struct DecodeConfig {
   size_t lds_bytes;  // dynamic LDS per workgroup
   size_t workspace_bytes;
 };
-// extra_lds: bytes a launch stages after the activations (fp16 NF4: its level-pair table)
+// extra_lds: bytes a launch stages after the activations (NF4: its level-pair table)
 DecodeConfig decode_config(int M, int K, int N, int group_size, bool glu, size_t extra_lds = 0);
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

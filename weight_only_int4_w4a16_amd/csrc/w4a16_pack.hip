@@ -46,6 +46,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const u4_t* __restrict__ p
                                                       const uint16_t* __restrict__ codebook,
                                                       int K, int N, int KC, int gs,
                                                       uint16_t* __restrict__ out, size_t total) {
+  __shared__ uint32_t ptab[kNf4PairEntries];  // NF4: the level-pair table of the GEMM kernels
+  if (NF4) {
+    nf4_pair_table_fill(ptab, codebook);
+    __syncthreads();
+  }
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= total) return;
   const int lane = (int)(t & 63);
@@ -54,8 +59,6 @@ __global__ __launch_bounds__(256) void dequant_kernel(const u4_t* __restrict__ p
   const int nt = (int)(blk / KC);
   const int n = nt * 16 + (lane & 15);
   const u4_t b = packed[t];
-  Nf4Lut lut;
-  if (NF4) lut = load_nf4_lut(codebook);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int k0 = kc * 128 + j * 32 + (lane >> 4) * 8;
@@ -67,10 +70,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(const u4_t* __restrict__ p
     u4_t d;
     if (NF4) {
       if (ACT == ACT_F16) {
-        d = __builtin_bit_cast(u4_t, dequant_word_nf4_f16(b[j], lut, as_h2(sbits * 0x00010001u)));
+        d = __builtin_bit_cast(u4_t, dequant_word_nf4_f16_tab(b[j], ptab, as_h2(sbits * 0x00010001u)));
       } else {
         const float a = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
-        d = __builtin_bit_cast(u4_t, dequant_word_nf4_bf16(b[j], lut, a));
+        d = __builtin_bit_cast(u4_t, dequant_word_nf4_bf16_tab(b[j], ptab, a));
       }
     } else {
       const uint32_t z = qzeros ? (qzeros[(size_t)g * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu
