@@ -145,7 +145,16 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     from weight_only_int4_w4a16_amd import kernel_name
     assert kernel_name(16, 4096, 28672, 128).startswith("w4a16_decode")    # x fits in LDS
     assert kernel_name(16, 14336, 4096, 128).startswith("w4a16_decode")    # K N < 2^27
-    assert kernel_name(16, 8192, 10240, 128).startswith("w4a16_decode")
+    # 4..16 rows where one round of skinny workgroups fills more than half the chip (K <= 8192):
+    # skinny from 8 rows (g128), 4 (groups of 32 or 64, NF4 blocks of 64)
+    assert kernel_name(16, 8192, 10240, 128).startswith("w4a16_skinny")   # 160 column tiles
+    assert kernel_name(8, 4096, 14336, 128).startswith("w4a16_skinny")
+    assert kernel_name(7, 4096, 14336, 128).startswith("w4a16_decode")
+    assert kernel_name(4, 4096, 14336, 32).startswith("w4a16_skinny")
+    assert kernel_name(3, 4096, 14336, 32).startswith("w4a16_decode")
+    assert kernel_name(4, 4096, 14336, 64).startswith("w4a16_skinny")
+    assert kernel_name(16, 8192, 8192, 128).startswith("w4a16_decode")    # 128 column tiles
+    assert kernel_name(8, 16384, 14336, 128).startswith("w4a16_decode")   # deeper than 8192
     assert kernel_name(11, 8192, 57344, 128).startswith("w4a16_decode")    # fewer than 12 rows
     # x beyond the decode kernel's LDS: skinny up to 8192 deep, batched beyond
     assert kernel_name(12, 8192, 57344, 128).startswith("w4a16_skinny")
@@ -202,8 +211,8 @@ def test_kernel_name_and_strings(L):
     assert kernel_name(0, 4096, 4096, 128) == "none"
     assert kernel_name(16, 4096, 4096, 128).startswith("w4a16_decode")
     # decode parity shapes that run persistent workgroups (256 compute units)
-    for M, K, N, g in ((16, 4096, 9216, 128), (13, 3968, 9248, 128), (12, 4224, 8208, 64),
-                       (15, 2080, 12304, 32), (12, 4096, 8208, 128), (8, 4096, 16400, 32),
+    for M, K, N, g in ((16, 4096, 16416, 128), (13, 3968, 16432, 128), (12, 4224, 16400, 64),
+                       (15, 2080, 16400, 32), (12, 4096, 16416, 128), (8, 4096, 16400, 32),
                        (16, 4096, 28672, 128)):
         assert kernel_name(M, K, N, g).endswith("_persist"), (M, K, N, g)
     assert not kernel_name(1, 4096, 28672, 128).endswith("_persist")

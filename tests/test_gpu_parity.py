@@ -98,12 +98,17 @@ SMALL = [
     (50, 8192, 32, 128, "f16", "asym"),
     # persistent decode workgroups (more tiles than resident slots, x staged once): one and
     # two strips per tile, waves with one group and with several, a ragged K, g32
-    (16, 4096, 9216, 128, "f16", "asym"),
-    (13, 3968, 9248, 128, "bf16", "asym"),
-    (12, 4224, 8208, 64, "bf16", "sym"),
-    (15, 2080, 12304, 32, "f16", "asym"),
-    (12, 4096, 8208, 128, "f16", "sym"),
+    (16, 4096, 16416, 128, "f16", "asym"),
+    (13, 3968, 16432, 128, "bf16", "asym"),
+    (12, 4224, 16400, 64, "bf16", "sym"),
+    (15, 2080, 16400, 32, "f16", "asym"),
+    (12, 4096, 16416, 128, "f16", "sym"),
     (8, 4096, 16400, 32, "f16", "asym"),
+    # 4..16 rows on the skinny kernel (one round of workgroups filling more than half the chip)
+    (4, 2048, 8704, 32, "f16", "asym"),
+    (5, 1024, 9216, 64, "f16", "nf4"),
+    (8, 4096, 10240, 128, "bf16", "sym"),
+    (4, 2048, 12288, 64, "bf16", "nf4"),
     # groups of 32 and 64 with four-block pipeline groups (one scale and zero word per block
     # and strip, shared between the lanes of a column): waves with several groups, a ragged
     # last group, two-strip SwiGLU-free tiles at g128 beside them

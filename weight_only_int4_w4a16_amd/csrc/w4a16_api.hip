@@ -89,6 +89,19 @@ Path choose_path(const GemmArgs& a) {
     // 129..256 rows: one round of 64-row tiles that fills at least half the chip
     return a.K <= 4096 && wgs <= cus && 2 * wgs > cus ? PATH_SKINNY : PATH_TILED;
   }
+  // 4..16 rows where one round of skinny workgroups fills more than half the chip: the skinny
+  // kernel from the row count where the decode kernel's cost per row overtakes it, earlier for
+  // the dearer dequantizations of groups of 32 or 64 (and NF4's 64-blocks) (4096x14336: NF4 at
+  // M=4/8/16 16.0/17.3/19.3 -> 12.7/12.7/12.8 us; g32 at M=4/8/16 13.0/15.7/18.4 ->
+  // 12.2/12.2/12.3; g128 at M=8/16 11.7/13.8 -> 11.6/11.8, 8192x10240 at M=8 17.4 -> 15.2).
+  // Fewer column tiles (4096x4096, 8192x8192, 14336x4096) or more (4096x28672) keep the
+  // decode kernel. The rule reads the group size only, so the name the logging call reports
+  // for a shape is the kernel that runs.
+  {
+    const long long cus = w4a16::device_cu_count();
+    const int from = a.group_size <= 64 ? 4 : 8;
+    if (a.M >= from && a.K <= 8192 && 2 * col_tiles > cus && col_tiles <= cus) return PATH_SKINNY;
+  }
   if (a.M < 12 || kn < (1LL << 27)) return PATH_DECODE;
   if (w4a16::decode_config(a.M, a.K, a.N, a.group_size, a.glu).x_in_lds) return PATH_DECODE;
   return a.K <= 8192 ? PATH_SKINNY : PATH_TILED;
