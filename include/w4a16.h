@@ -85,11 +85,13 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group_size);
  *   workspace [in/out] >= w4a16_workspace_bytes(M, K, N, group_size) bytes, 256-byte
  *                   aligned (may be NULL when that size is 0)
  * M = 0 is a no-op. Results are deterministic: partial sums are combined in a fixed
- * order, never with floating-point atomics. M <= 16 runs the memory-bound decode kernel,
- * M > 16 the batched MFMA kernel, with two exceptions: 12 <= M <= 16 on weights with
- * K * N >= 2^27 whose activations do not fit the decode kernel's LDS staging go to the batched
- * kernel, and 17 <= M <= 32 on weights with K * N <= 2^24 stay on the decode kernel (one launch
- * per 16 rows). w4a16_kernel_name names the kernel a shape gets. */
+ * order, never with floating-point atomics. Three kernels share the work, chosen by shape
+ * (w4a16_kernel_name names the one a shape gets): the memory-bound decode kernel for up to 16
+ * rows (and up to 32 on weights with K * N < 2^24, one launch per 16 rows); the skinny kernel
+ * (K split across the waves of one workgroup) for about 4..256 rows on weights at most 8192
+ * deep whose 64-column workgroups fill the chip in one to four launch rounds; the batched MFMA
+ * kernel for the other shapes past 16 rows, and for 12..16 rows on weights with K * N >= 2^27
+ * deeper than 8192 whose activations do not fit the decode kernel's LDS staging. */
 w4a16_status w4a16_gemm(const void* x, int M, int K, int N, w4a16_dtype act,
                         const int32_t* packed, const void* scales, const int32_t* qzeros,
                         int group_size, void* out, w4a16_dtype out_dtype, void* workspace,
