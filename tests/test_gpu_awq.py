@@ -68,6 +68,9 @@ SMALL = [
     (20, 4096, 4128, 128, "bf16", "asym"),  # batched 64x256 tile, just past 16 rows
     (40, 2080, 512, 32, "bf16", "sym"),
     (130, 2048, 64, 128, "f16", "asym"),    # batched, K split in two
+    (8, 4096, 10240, 128, "f16", "asym"),   # skinny at 8 rows: x scaled into the workspace
+    (24, 2048, 16400, 64, "bf16", "sym"),   # skinny, 32-row tile, ragged column tile
+    (96, 1024, 8320, 128, "f16", "asym"),   # skinny, 128-row tile
 ]
 
 

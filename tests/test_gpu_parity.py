@@ -203,6 +203,9 @@ SWIGLU = [
     (513, 2080, 16416, 32, "bf16", "asym"),  # batched 128x512
     (48, 1024, 96, 64, "f16", "nf4"),        # skinny, two row tiles, ragged gate half
     (33, 2176, 160, 128, "bf16", "sym"),     # skinny, ragged K
+    (8, 2048, 10240, 128, "bf16", "sym"),    # skinny at 8 rows (its workgroups fill the chip)
+    (96, 1024, 8320, 128, "f16", "asym"),    # skinny, 128-row tile
+    (150, 1024, 4096, 64, "f16", "nf4"),     # skinny past 128 rows, ragged last row tile
 ]
 
 
