@@ -186,6 +186,18 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     assert kernel_name(257, 4096, 4096, 128).startswith("w4a16_tiled")
     assert kernel_name(200, 2048, 64, 128).startswith("w4a16_tiled")      # 4 workgroups
     assert kernel_name(192, 4096, 14336, 128).startswith("w4a16_tiled")
+    # up to 6144-deep K the skinny kernel keeps one launch round at 33..256 rows, and from 224
+    # rows takes one round of 128-row tiles on 3072..6144-deep weights
+    assert kernel_name(96, 5120, 5120, 128) == "w4a16_skinny_64x64"
+    assert kernel_name(128, 5120, 13824, 128) == "w4a16_skinny_128x64"
+    assert kernel_name(160, 5120, 5120, 128) == "w4a16_skinny_64x64"
+    assert kernel_name(256, 4096, 6144, 128) == "w4a16_skinny_128x64"
+    assert kernel_name(256, 2048, 8192, 128).startswith("w4a16_tiled")     # K < 3072
+    assert kernel_name(96, 8192, 10240, 128).startswith("w4a16_tiled")     # K > 6144
+    # 16 rows with a quarter to a half of the chip's worth of column tiles, K 3072..6144
+    assert kernel_name(16, 5120, 5120, 128).startswith("w4a16_skinny")
+    assert kernel_name(12, 5120, 5120, 128).startswith("w4a16_decode")
+    assert kernel_name(16, 2048, 8192, 128).startswith("w4a16_decode")
 
 
 def test_nf4_requires_codebook(L):

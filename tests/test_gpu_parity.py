@@ -152,6 +152,12 @@ SMALL = [
     (96, 512, 8256, 128, "f16", "asym"),
     (80, 1152, 8704, 32, "bf16", "sym"),
     (128, 640, 8256, 64, "f16", "nf4"),
+    # skinny kernel on 4608-deep weights with 128-row tiles, from 224 rows on 128-row tiles
+    # (two of them, the second ragged), 16 rows on a fifth of the chip's worth of column tiles
+    (100, 4608, 8320, 128, "f16", "asym"),
+    (240, 3584, 6144, 64, "f16", "nf4"),
+    (176, 5120, 4096, 128, "bf16", "asym"),
+    (16, 3072, 5120, 32, "f16", "sym"),
     # skinny kernel past 128 rows (one round of 64-row tiles): a ragged last row tile
     (160, 768, 3072, 128, "f16", "asym"),
     (256, 1024, 4096, 64, "bf16", "nf4"),

@@ -65,10 +65,14 @@ Path forced_path() {
 // (above). Where 64-row tiles would take more than one round at 65-128 rows and K <= 4096, its
 // 128-row tiles (four waves, one per SIMD) still win (4096x14336 at M=96: 26.0 against 30.1 us,
 // M=128: 27.8 against 32.0 us; at M=192 and 256 they lose, 49.4 and 53.6 against 34.1 and
-// 39.6 us). Past 128 rows the skinny kernel keeps only launches of one round of 64-row tiles
-// that fill at least half the chip (smaller ones are unmeasured). At 33+ rows on 8192-deep K with fewer than 160 column tiles the batched kernel's
-// split K wins (8192x8192 at M=64: 21.9 against 26.4 us), and so it does for deeper K, wider N
-// and more rows.
+// 39.6 us). Up to 6144-deep K the same holds without the column-tile condition (5120x5120 at
+// M=96/128: 19.5/19.4 against 21.7/23.1 us; 5120x13824 at M=96: 30.5 against 34.0). Past 128
+// rows the skinny kernel takes one round of 64-row tiles filling at least half the chip
+// (5120x5120 at M=160/192: 21.4/20.5 against 28.2/27.1 us), and from 224 rows one round of
+// 128-row tiles on 3072..6144-deep weights (4096x6144 at M=256: 25.8 against 29.3 us;
+// 2048x8192 loses, 21.1 against 20.4). At 33+ rows on 8192-deep K with fewer than 160 column
+// tiles the batched kernel's split K wins (8192x8192 at M=64: 21.9 against 26.4 us), and so it
+// does for deeper K, wider N and more rows.
 Path choose_path(const GemmArgs& a) {
   const Path f = forced_path();
   if (f != PATH_AUTO) return f;
@@ -80,14 +84,17 @@ Path choose_path(const GemmArgs& a) {
     if (a.K > 8192) return PATH_TILED;
     if (a.M <= 32) return col_tiles <= 1024 ? PATH_SKINNY : PATH_TILED;
     const long long cus = w4a16::device_cu_count();
-    const long long wgs = col_tiles * ((a.M + 63) / 64);  // 64-row tiles
+    const long long wgs = col_tiles * ((a.M + 63) / 64);    // 64-row tiles
+    const long long wgs4 = col_tiles * ((a.M + 127) / 128);  // 128-row tiles
+    const bool mid_k = a.K <= 6144;
     if (a.M <= 128) {
-      if (wgs <= cus && (a.K <= 4096 || col_tiles >= 160)) return PATH_SKINNY;
-      // 128-row tiles
-      return a.K <= 4096 && col_tiles * ((a.M + 127) / 128) <= cus ? PATH_SKINNY : PATH_TILED;
+      if (wgs <= cus && (mid_k || col_tiles >= 160)) return PATH_SKINNY;
+      return mid_k && wgs4 <= cus ? PATH_SKINNY : PATH_TILED;
     }
-    // 129..256 rows: one round of 64-row tiles that fills at least half the chip
-    return a.K <= 4096 && wgs <= cus && 2 * wgs > cus ? PATH_SKINNY : PATH_TILED;
+    // 129..256 rows: one round of 64-row tiles that fills at least half the chip, or (from 224
+    // rows, 3072..6144-deep weights) one round of 128-row tiles
+    if (mid_k && wgs <= cus && 2 * wgs > cus) return PATH_SKINNY;
+    return a.M >= 224 && a.K >= 3072 && mid_k && wgs4 <= cus ? PATH_SKINNY : PATH_TILED;
   }
   // 4..16 rows where one round of skinny workgroups fills more than half the chip: the skinny
   // kernel from the row count where the decode kernel's cost per row overtakes it, earlier for
@@ -97,10 +104,15 @@ Path choose_path(const GemmArgs& a) {
   // Fewer column tiles (4096x4096, 8192x8192, 14336x4096) or more (4096x28672) keep the
   // decode kernel. The rule reads the group size only, so the name the logging call reports
   // for a shape is the kernel that runs.
+  // With a quarter to a half of the chip's worth of column tiles, the skinny kernel wins only
+  // from 16 rows, on 3072..6144-deep weights (5120x5120 at M=16: 13.0 -> 11.4 us; 3072x8192
+  // 9.6 -> 8.9; 2048x8192 stays: 6.0 against 6.3).
   {
     const long long cus = w4a16::device_cu_count();
-    const int from = a.group_size <= 64 ? 4 : 8;
-    if (a.M >= from && a.K <= 8192 && 2 * col_tiles > cus && col_tiles <= cus) return PATH_SKINNY;
+    if (a.K <= 8192 && col_tiles <= cus) {
+      if (2 * col_tiles > cus && a.M >= (a.group_size <= 64 ? 4 : 8)) return PATH_SKINNY;
+      if (4 * col_tiles > cus && a.M >= 16 && a.K >= 3072 && a.K <= 6144) return PATH_SKINNY;
+    }
   }
   if (a.M < 12 || kn < (1LL << 27)) return PATH_DECODE;
   if (w4a16::decode_config(a.M, a.K, a.N, a.group_size, a.glu).x_in_lds) return PATH_DECODE;
