@@ -178,7 +178,8 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     # 65..128 rows where 64-row tiles would take two rounds: 128-row tiles (K <= 4096)
     assert kernel_name(96, 4096, 14336, 128) == "w4a16_skinny_128x64"     # 224 workgroups
     assert kernel_name(128, 4096, 14336, 128) == "w4a16_skinny_128x64"
-    assert kernel_name(128, 8192, 14336, 128).startswith("w4a16_tiled")   # deeper than 4096
+    assert kernel_name(128, 8192, 14336, 128) == "w4a16_skinny_128x64"    # 8192 deep, one round
+    assert kernel_name(128, 8192, 28672, 128).startswith("w4a16_tiled")   # 448 workgroups
     assert kernel_name(128, 4096, 4096, 128) == "w4a16_skinny_64x64"      # one round of 64 rows
     # 129..256 rows: one round of 64-row tiles filling at least half the chip, K <= 4096
     assert kernel_name(129, 4096, 4096, 128) == "w4a16_skinny_64x64"      # 192 workgroups
@@ -193,11 +194,19 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     assert kernel_name(160, 5120, 5120, 128) == "w4a16_skinny_64x64"
     assert kernel_name(256, 4096, 6144, 128) == "w4a16_skinny_128x64"
     assert kernel_name(256, 2048, 8192, 128).startswith("w4a16_tiled")     # K < 3072
-    assert kernel_name(96, 8192, 10240, 128).startswith("w4a16_tiled")     # K > 6144
+    assert kernel_name(96, 8192, 10240, 128) == "w4a16_skinny_128x64"     # 128-row tiles to K 8192
+    assert kernel_name(64, 8192, 8192, 128).startswith("w4a16_tiled")      # 64-row tiles: K > 6144
     # 16 rows with a quarter to a half of the chip's worth of column tiles, K 3072..6144
     assert kernel_name(16, 5120, 5120, 128).startswith("w4a16_skinny")
     assert kernel_name(12, 5120, 5120, 128).startswith("w4a16_decode")
     assert kernel_name(16, 2048, 8192, 128).startswith("w4a16_decode")
+    # groups of 32/64: the quarter-to-half band from 12 rows, one to two rounds from 4 rows
+    assert kernel_name(12, 4096, 6144, 32).startswith("w4a16_skinny")
+    assert kernel_name(8, 4096, 6144, 32).startswith("w4a16_decode")
+    assert kernel_name(12, 2048, 8192, 32).startswith("w4a16_decode")    # K < 3072
+    assert kernel_name(4, 8192, 28672, 32).startswith("w4a16_skinny")    # 448 column tiles
+    assert kernel_name(4, 8192, 28672, 128).startswith("w4a16_decode")
+    assert kernel_name(4, 8192, 36864, 32).startswith("w4a16_decode")    # 576 column tiles
 
 
 def test_nf4_requires_codebook(L):
@@ -223,8 +232,8 @@ def test_kernel_name_and_strings(L):
     assert kernel_name(0, 4096, 4096, 128) == "none"
     assert kernel_name(16, 4096, 4096, 128).startswith("w4a16_decode")
     # decode parity shapes that run persistent workgroups (256 compute units)
-    for M, K, N, g in ((16, 4096, 16416, 128), (13, 3968, 16432, 128), (12, 4224, 16400, 64),
-                       (15, 2080, 16400, 32), (12, 4096, 16416, 128), (8, 4096, 16400, 32),
+    for M, K, N, g in ((16, 4096, 16416, 128), (13, 3968, 16432, 128), (12, 4224, 32784, 64),
+                       (15, 2080, 32784, 32), (12, 4096, 16416, 128), (8, 4096, 32784, 32),
                        (16, 4096, 28672, 128)):
         assert kernel_name(M, K, N, g).endswith("_persist"), (M, K, N, g)
     assert not kernel_name(1, 4096, 28672, 128).endswith("_persist")

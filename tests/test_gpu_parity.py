@@ -100,15 +100,17 @@ SMALL = [
     # two strips per tile, waves with one group and with several, a ragged K, g32
     (16, 4096, 16416, 128, "f16", "asym"),
     (13, 3968, 16432, 128, "bf16", "asym"),
-    (12, 4224, 16400, 64, "bf16", "sym"),
-    (15, 2080, 16400, 32, "f16", "asym"),
+    (12, 4224, 32784, 64, "bf16", "sym"),
+    (15, 2080, 32784, 32, "f16", "asym"),
     (12, 4096, 16416, 128, "f16", "sym"),
-    (8, 4096, 16400, 32, "f16", "asym"),
+    (8, 4096, 32784, 32, "f16", "asym"),
     # 4..16 rows on the skinny kernel (one round of workgroups filling more than half the chip)
     (4, 2048, 8704, 32, "f16", "asym"),
     (5, 1024, 9216, 64, "f16", "nf4"),
     (8, 4096, 10240, 128, "bf16", "sym"),
     (4, 2048, 12288, 64, "bf16", "nf4"),
+    (4, 2048, 20480, 32, "f16", "asym"),     # groups of 32 over one to two rounds of tiles
+    (12, 4096, 6144, 64, "bf16", "nf4"),     # a quarter to a half of the chip's column tiles
     # groups of 32 and 64 with four-block pipeline groups (one scale and zero word per block
     # and strip, shared between the lanes of a column): waves with several groups, a ragged
     # last group, two-strip SwiGLU-free tiles at g128 beside them
@@ -198,7 +200,7 @@ SWIGLU = [
     (16, 1024, 128, 64, "f16", "sym"),
     (5, 14336, 64, 64, "f16", "asym"),       # x from global (too large for LDS at 5 rows)
     (12, 4096, 16416, 128, "f16", "asym"),   # persistent, one group per wave
-    (9, 4224, 16448, 64, "bf16", "nf4"),     # persistent, several groups per wave
+    (9, 4224, 32832, 64, "bf16", "nf4"),     # persistent, several groups per wave
     (2, 1024, 96, 64, "bf16", "nf4"),
     (4, 1024, 96, 64, "f16", "nf4"),         # fp16 NF4, x in LDS in nibble order, SwiGLU tile
     (17, 512, 64, 128, "bf16", "asym"),      # decode, two launches (16 + 1 rows)

@@ -65,7 +65,8 @@ Path forced_path() {
 // (above). Where 64-row tiles would take more than one round at 65-128 rows and K <= 4096, its
 // 128-row tiles (four waves, one per SIMD) still win (4096x14336 at M=96: 26.0 against 30.1 us,
 // M=128: 27.8 against 32.0 us; at M=192 and 256 they lose, 49.4 and 53.6 against 34.1 and
-// 39.6 us). Up to 6144-deep K the same holds without the column-tile condition (5120x5120 at
+// 39.6 us), also on 8192-deep K (8192x10240 at M=96/128: a tie at g128, 8-12% for g32, NF4
+// and bf16). Up to 6144-deep K the 64-row rule holds without the column-tile condition (5120x5120 at
 // M=96/128: 19.5/19.4 against 21.7/23.1 us; 5120x13824 at M=96: 30.5 against 34.0). Past 128
 // rows the skinny kernel takes one round of 64-row tiles filling at least half the chip
 // (5120x5120 at M=160/192: 21.4/20.5 against 28.2/27.1 us), and from 224 rows one round of
@@ -89,7 +90,8 @@ Path choose_path(const GemmArgs& a) {
     const bool mid_k = a.K <= 6144;
     if (a.M <= 128) {
       if (wgs <= cus && (mid_k || col_tiles >= 160)) return PATH_SKINNY;
-      return mid_k && wgs4 <= cus ? PATH_SKINNY : PATH_TILED;
+      // 128-row tiles (K <= 8192) where 64-row tiles would take a second round
+      return wgs > cus && wgs4 <= cus ? PATH_SKINNY : PATH_TILED;
     }
     // 129..256 rows: one round of 64-row tiles that fills at least half the chip, or (from 224
     // rows, 3072..6144-deep weights) one round of 128-row tiles
@@ -107,12 +109,22 @@ Path choose_path(const GemmArgs& a) {
   // With a quarter to a half of the chip's worth of column tiles, the skinny kernel wins only
   // from 16 rows, on 3072..6144-deep weights (5120x5120 at M=16: 13.0 -> 11.4 us; 3072x8192
   // 9.6 -> 8.9; 2048x8192 stays: 6.0 against 6.3).
+  // Groups of 32 or 64 (NF4 64-blocks) make the decode kernel's rows dearer still: there the
+  // skinny kernel also wins from 12 rows in the quarter-to-half band (5120x5120 g32 at M=12:
+  // 14.3 -> 12.5 us; NF4 3072x8192 12.0 -> 10.2; at 8 rows it wins on some shapes and loses
+  // up to 18% on others), and from 4 rows over one to two rounds of column tiles (8192x28672
+  // g32 at M=4/8: 40.8/45.6 -> 36.7/37.4 us; NF4 45.2/45.8 -> 38.4/40.0). Measured against
+  // the previous rules in one run over an 11-shape x 13-batch grid: g32 -0.5%, NF4 -0.9%,
+  // bf16 -0.5% in total, g128 unchanged.
   {
     const long long cus = w4a16::device_cu_count();
+    const bool dear = a.group_size <= 64;
     if (a.K <= 8192 && col_tiles <= cus) {
-      if (2 * col_tiles > cus && a.M >= (a.group_size <= 64 ? 4 : 8)) return PATH_SKINNY;
-      if (4 * col_tiles > cus && a.M >= 16 && a.K >= 3072 && a.K <= 6144) return PATH_SKINNY;
+      if (2 * col_tiles > cus && a.M >= (dear ? 4 : 8)) return PATH_SKINNY;
+      if (4 * col_tiles > cus && a.K >= 3072 && a.K <= 6144 && a.M >= (dear ? 12 : 16))
+        return PATH_SKINNY;
     }
+    if (dear && a.K <= 8192 && col_tiles > cus && col_tiles <= 2 * cus && a.M >= 4) return PATH_SKINNY;
   }
   if (a.M < 12 || kn < (1LL << 27)) return PATH_DECODE;
   if (w4a16::decode_config(a.M, a.K, a.N, a.group_size, a.glu).x_in_lds) return PATH_DECODE;
