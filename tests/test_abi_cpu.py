@@ -194,6 +194,9 @@ def test_dispatch_between_decode_and_batched_kernels(L):
     assert kernel_name(160, 5120, 5120, 128) == "w4a16_skinny_64x64"
     assert kernel_name(256, 4096, 6144, 128) == "w4a16_skinny_128x64"
     assert kernel_name(256, 2048, 8192, 128).startswith("w4a16_tiled")     # K < 3072
+    assert kernel_name(160, 4096, 6144, 128) == "w4a16_skinny_128x64"     # from 160 rows, K 4096
+    assert kernel_name(192, 3072, 8192, 128).startswith("w4a16_tiled")     # K < 4096 below 224 rows
+    assert kernel_name(144, 4096, 6144, 128).startswith("w4a16_tiled")
     assert kernel_name(96, 8192, 10240, 128) == "w4a16_skinny_128x64"     # 128-row tiles to K 8192
     assert kernel_name(64, 8192, 8192, 128).startswith("w4a16_tiled")      # 64-row tiles: K > 6144
     # 16 rows with a quarter to a half of the chip's worth of column tiles, K 3072..6144

@@ -158,6 +158,7 @@ SMALL = [
     # (two of them, the second ragged), 16 rows on a fifth of the chip's worth of column tiles
     (100, 4608, 8320, 128, "f16", "asym"),
     (240, 3584, 6144, 64, "f16", "nf4"),
+    (168, 4096, 6208, 32, "bf16", "asym"),
     (176, 5120, 4096, 128, "bf16", "asym"),
     (16, 3072, 5120, 32, "f16", "sym"),
     # skinny kernel past 128 rows (one round of 64-row tiles): a ragged last row tile

@@ -69,9 +69,11 @@ Path forced_path() {
 // and bf16). Up to 6144-deep K the 64-row rule holds without the column-tile condition (5120x5120 at
 // M=96/128: 19.5/19.4 against 21.7/23.1 us; 5120x13824 at M=96: 30.5 against 34.0). Past 128
 // rows the skinny kernel takes one round of 64-row tiles filling at least half the chip
-// (5120x5120 at M=160/192: 21.4/20.5 against 28.2/27.1 us), and from 224 rows one round of
-// 128-row tiles on 3072..6144-deep weights (4096x6144 at M=256: 25.8 against 29.3 us;
-// 2048x8192 loses, 21.1 against 20.4). At 33+ rows on 8192-deep K with fewer than 160 column
+// (5120x5120 at M=160/192: 21.4/20.5 against 28.2/27.1 us), and one round of 128-row tiles
+// from 224 rows on 3072..6144-deep weights (4096x6144 at M=256: 25.8 against 29.3 us;
+// 2048x8192 loses, 21.1 against 20.4) and from 160 rows on 4096..6144-deep ones (4096x6144
+// at M=160/192: g128 -2/-4%, g32 -9/-12%, NF4 -10/-14%, bf16 -13/-17%; at 3072x8192 the
+// batched kernel still wins by 7-9% for g128 and ties for g32 and NF4). At 33+ rows on 8192-deep K with fewer than 160 column
 // tiles the batched kernel's split K wins (8192x8192 at M=64: 21.9 against 26.4 us), and so it
 // does for deeper K, wider N and more rows.
 Path choose_path(const GemmArgs& a) {
@@ -93,10 +95,11 @@ Path choose_path(const GemmArgs& a) {
       // 128-row tiles (K <= 8192) where 64-row tiles would take a second round
       return wgs > cus && wgs4 <= cus ? PATH_SKINNY : PATH_TILED;
     }
-    // 129..256 rows: one round of 64-row tiles that fills at least half the chip, or (from 224
-    // rows, 3072..6144-deep weights) one round of 128-row tiles
+    // 129..256 rows: one round of 64-row tiles that fills at least half the chip, or one round
+    // of 128-row tiles from 160 rows on 4096..6144-deep weights and from 224 rows on 3072-deep
     if (mid_k && wgs <= cus && 2 * wgs > cus) return PATH_SKINNY;
-    return a.M >= 224 && a.K >= 3072 && mid_k && wgs4 <= cus ? PATH_SKINNY : PATH_TILED;
+    const bool deep_enough = a.M >= 224 ? a.K >= 3072 : a.M >= 160 && a.K >= 4096;
+    return deep_enough && mid_k && wgs4 <= cus ? PATH_SKINNY : PATH_TILED;
   }
   // 4..16 rows where one round of skinny workgroups fills more than half the chip: the skinny
   // kernel from the row count where the decode kernel's cost per row overtakes it, earlier for
