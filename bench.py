@@ -557,6 +557,9 @@ def main() -> int:
     ap.add_argument("--sweep-configs", default=None,
                     help="--sweep: only the configs whose name contains one of these "
                          "comma-separated strings (e.g. 'g32,nf4')")
+    ap.add_argument("--cpu-baselines", action="store_true",
+                    help="only the CPU oracle, timed per benchmark workload and batch size (host "
+                         "cores only; one JSON line per (workload, M)), instead of the GPU bench")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (x4), the known-size reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -567,6 +570,20 @@ def main() -> int:
               "(each GPU of a column or row split would run these kernels on its own shard; "
               "the cross-GPU exchange is not part of it)", file=sys.stderr)
         return 2
+
+    if args.cpu_baselines:
+        # every benchmark workload at M=1 and at its own batch size: the oracle's dequant and
+        # fp64 matmul timed separately per linear (see cpu_baseline); no GPU is used
+        for name, base in WORKLOADS.items():
+            for M in sorted({1, base["m"]}):
+                spec = dict(base)
+                spec["name"] = name
+                cb = cpu_baseline(spec, M)
+                flops = sum(2.0 * M * K * N for K, N in spec["shapes"]) * spec["layers"]
+                print(json.dumps({"workload": name, "M": M, "cpu_baseline": cb,
+                                  "GFLOP/s": round(flops / cb["step_s_projected"] / 1e9, 3)}),
+                      flush=True)
+        return 0
 
     import torch
 
