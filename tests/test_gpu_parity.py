@@ -419,6 +419,11 @@ FULL.append((129, 4224, 28688, 64, "bf16", "asym"))
 # 12..16 rows on large weights whose x exceeds the decode kernel's LDS: the batched kernel
 FULL.append((16, 8192, 57344, 128, "f16", "sym"))
 FULL.append((12, 28672, 8192, 128, "bf16", "asym"))
+# the skinny kernel's wider bands at full size: groups of 32 over two rounds of column tiles at
+# 8 rows, 128-row tiles on 8192-deep K, 128-row tiles from 160 rows (NF4)
+FULL.append((8, 8192, 28672, 32, "f16", "asym"))
+FULL.append((96, 8192, 10240, 128, "bf16", "asym"))
+FULL.append((192, 4096, 6144, 64, "f16", "nf4"))
 
 
 @pytest.mark.parametrize("M,K,N,g,act,fmt", FULL)
