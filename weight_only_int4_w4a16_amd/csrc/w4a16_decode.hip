@@ -122,9 +122,13 @@ DecodeConfig choose(int M, int K, int N, int group_size, bool x_in_lds, bool glu
       if (wg_per_cu < 1) wg_per_cu = 1;
       const long rounds = ceil_div(c.tiles, cus * wg_per_cu);
       const long cost = rounds * (ceil_div(c.slice, D) + 2);
-      // ties: the choice that keeps more compute units busy
-      const int busy = c.tiles < cus ? c.tiles : cus;
-      const int best_busy = best.tiles < cus ? best.tiles : cus;
+      // ties: the choice that keeps more compute units busy, counting three quarters of them
+      // as all, so that the wider tile (tried first) keeps a tie there (4096x6144: two-strip
+      // tiles on 192 units against one-strip tiles on 256 measured 5.11 / 5.49 against 5.21 /
+      // 6.48 us at M=1 / 4; with 128 two-strip tiles the one-strip tiles stay faster)
+      auto busy_of = [&](int tiles) { const int b = tiles < cus ? tiles : cus; return 4 * b >= 3 * cus ? cus : b; };
+      const int busy = busy_of(c.tiles);
+      const int best_busy = busy_of(best.tiles);
       if (best_cost < 0 || cost < best_cost || (cost == best_cost && busy > best_busy)) {
         best = c;
         best_cost = cost;
